@@ -1,0 +1,245 @@
+"""Pins of the CPU oracle against what the mathematics fixes (CPU only).
+
+Each test checks the oracle against something other than itself: a library
+routine (torch SDPA, numpy reductions), a closed form, a brute-force
+materialisation, or an invariant the method states.  Together they are
+chosen so that a dropped term, a wrong sign, a wrong weight or a transposed
+operand in the oracle fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from free_dynamic_sparse_amd import synth
+from oracle import solattn_ref as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sdpa(q, k, v, scale, mask=None):
+    """torch's scaled-dot-product attention on CPU in float64 (library routine)."""
+    t = lambda x: torch.as_tensor(np.asarray(x, np.float64))[None, None]
+    m = None if mask is None else torch.as_tensor(mask)[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m,
+                                                         scale=scale)
+    return o[0, 0].numpy()
+
+
+def small(L=1000, d=64, block=64, seed=11, kind="iid", grid=None):
+    w = synth.Workload("t", B=1, H=1, L=L, d=d, block=block, chunk=16, seed=seed, kind=kind,
+                       grid=grid)
+    q, k, v = synth.make_head(w, 0, 0)
+    return w, q, k, v
+
+
+def phi_sf(beta):
+    """1 - Phi(beta) for the standard normal."""
+    return 0.5 * math.erfc(beta / math.sqrt(2.0))
+
+
+# ---------------------------------------------------------------- pooling
+
+@pytest.mark.parametrize("L", [4096, 1000, 65])
+def test_pool_matches_numpy_segment_reductions(L):
+    _, q, k, v = small(L=L)
+    block = 64
+    qbar, kbar, vhat = ref.pool(q, k, v, block)
+    starts = np.arange(0, L, block)
+    n = np.diff(np.append(starts, L)).astype(np.float64)
+    for x, got, is_mean in ((q, qbar, True), (k, kbar, True), (v, vhat, False)):
+        s = np.add.reduceat(x.astype(np.float64), starts, axis=0)
+        want = s / n[:, None] if is_mean else s
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(ref.block_sizes(L, block), n.astype(np.int64))
+
+
+# ---------------------------------------------------------------- moments
+
+@pytest.mark.parametrize("case", ["iid_ragged", "pos"])
+def test_row_stats_equal_bruteforce_proxy_rows(case):
+    if case == "iid_ragged":
+        w, q, k, v = small(L=1000)
+    else:
+        w, q, k, v = small(L=4096, d=128, block=128, kind="pos", grid=(1, 64, 64))
+    scale = 1.0 / math.sqrt(w.d)
+    qbar, kbar, _ = ref.pool(q, k, v, w.block)
+    m, cov = ref.key_moments(kbar)
+    mu, sigma = ref.row_stats(qbar, m, cov, scale)
+    shat = ref.proxy_scores(qbar, kbar, scale)
+    # brute force: materialise every proxy row and take numpy's mean / std (ddof=0)
+    np.testing.assert_allclose(mu, shat.mean(axis=1), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(sigma, shat.std(axis=1, ddof=0), rtol=1e-9, atol=1e-12)
+    # brute force of the moments themselves
+    np.testing.assert_allclose(m, kbar.mean(axis=0), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cov, np.cov(kbar.T, bias=True), rtol=1e-9, atol=1e-13)
+
+
+def test_thresholds_special_values():
+    mu = np.array([0.5, 1.0, -2.0])
+    sigma = np.array([1.0, 0.0, 2.0])
+    assert np.all(ref.thresholds(mu, sigma, -math.inf) == -np.inf)
+    assert np.all(ref.thresholds(mu, sigma, math.inf) == np.inf)
+    tau = ref.thresholds(mu, sigma, 1.5)
+    assert tau[0] == 2.0 and tau[1] == -np.inf and tau[2] == 1.0
+    with pytest.raises(ValueError):
+        ref.thresholds(mu, sigma, float("nan"))
+
+
+@pytest.mark.parametrize("beta", [0.5, 1.0, 1.5, 2.0])
+def test_mean_density_tracks_gaussian_tail(beta):
+    # iid N(0,1) Q and K: given Qbar_i, the proxy row is an iid Gaussian sample,
+    # so the mean selected density approaches rho_G(beta) = 1 - Phi(beta).
+    dens = []
+    for seed in range(12):
+        w = synth.Workload("t", B=1, H=1, L=4096, d=64, block=64, chunk=16, seed=100 + seed)
+        q, k, v = synth.make_head(w, 0, 0)
+        r = ref.solattn_head(q, k, v, beta, 64, rows=[])
+        dens.append(r.sel.mean())
+    assert abs(np.mean(dens) - phi_sf(beta)) <= 0.01
+
+
+def test_mean_density_tracks_gaussian_tail_long_row():
+    # N = 591 blocks (the Wan block count): tighter tolerance.
+    w = synth.Workload("t", B=1, H=1, L=591 * 128, d=128, block=128, chunk=32, seed=7)
+    q, k, v = synth.make_head(w, 0, 0)
+    r = ref.solattn_head(q, k, v, 1.0, 128, rows=[])
+    assert abs(r.sel.mean() - phi_sf(1.0)) <= 0.003
+
+
+def test_selection_invariances():
+    w, q, k, v = small(L=4096, d=64, block=64, kind="pos", grid=(1, 64, 64))
+    base = ref.solattn_head(q, k, v, 1.0, 64, rows=[])
+    # (a) any positive softmax scale gives the same selection
+    for s in (0.01, 1.0, 3.0):
+        r = ref.solattn_head(q, k, v, 1.0, 64, scale=s, rows=[])
+        band = np.abs(base.shat - base.tau[:, None]) < 1e-6 * base.sigma[:, None]
+        assert np.all((r.sel == base.sel) | band)
+    # (b) permuting key blocks (with their values) permutes the selection and
+    #     leaves every output unchanged
+    N = w.N
+    perm = np.random.default_rng(0).permutation(N)
+    kp = k.reshape(N, 64, -1)[perm].reshape(k.shape)
+    vp = v.reshape(N, 64, -1)[perm].reshape(v.shape)
+    full = ref.solattn_head(q, k, v, 1.0, 64)
+    permd = ref.solattn_head(q, kp, vp, 1.0, 64)
+    np.testing.assert_array_equal(permd.sel, full.sel[:, perm])
+    np.testing.assert_allclose(permd.out, full.out, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- streaming
+
+@pytest.mark.parametrize("chunk", [1, 5, 16, 64, 70])
+def test_streaming_selection_equals_full_row(chunk):
+    w, q, k, v = small(L=4000, d=64, block=64, kind="pos", grid=(1, 50, 80))
+    scale = 1.0 / 8.0
+    r = ref.solattn_head(q, k, v, 1.0, 64, rows=[])
+    s = ref.select_streaming(q, r.kbar, r.tau, 64, chunk, scale)
+    np.testing.assert_array_equal(s, r.sel)
+
+
+def test_tile_column_means_are_proxy_scores():
+    # The column means of the token-to-block tile (Eq. 11) are the proxy scores.
+    w, q, k, v = small(L=1000, d=64, block=64)
+    scale = 0.125
+    qbar, kbar, _ = ref.pool(q, k, v, 64)
+    shat = ref.proxy_scores(qbar, kbar, scale)
+    for i in range(w.N):
+        a, b = ref.block_range(w.L, 64, i)
+        tile = scale * (q[a:b].astype(np.float64) @ kbar.T)
+        np.testing.assert_allclose(tile.mean(axis=0), shat[i], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 64])
+@pytest.mark.parametrize("beta", [0.5, 1.0])
+def test_streaming_forward_equals_direct_forward(chunk, beta):
+    w, q, k, v = small(L=1500, d=64, block=64, kind="pos", grid=(1, 30, 50))
+    r = ref.solattn_head(q, k, v, beta, 64)
+    out, sel = ref.forward_streaming(q, k, v, r.tau, 64, chunk, r.scale)
+    np.testing.assert_array_equal(sel, r.sel)
+    np.testing.assert_allclose(out, r.out, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("L", [1000, 4096])
+def test_beta_minus_inf_is_dense_attention(L):
+    w, q, k, v = small(L=L)
+    r = ref.solattn_head(q, k, v, -math.inf, 64)
+    assert r.sel.all()
+    want = sdpa(q, k, v, r.scale)
+    np.testing.assert_allclose(r.out, want, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ref.dense(q, k, v, r.scale), want, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0, 2.0, math.inf])
+def test_block_constant_keys_make_the_approximation_exact(beta):
+    # If every key of block j equals Kbar_j, the zeroth-order term is exact, so
+    # the output is dense attention whatever is selected.  The ragged last
+    # block (n_j < block) checks the n_j weight; Vhat as a sum is checked too.
+    w, q, _, v = small(L=1000)
+    rng = np.random.default_rng(5)
+    kb = rng.standard_normal((w.N, w.d))
+    k = np.repeat(kb, 64, axis=0)[:w.L]
+    r = ref.solattn_head(q, k, v, beta, 64)
+    if beta not in (0.0, math.inf):
+        assert 0 < r.sel.mean() < 1
+    np.testing.assert_allclose(r.out, sdpa(q, k, v, r.scale), rtol=1e-10, atol=1e-12)
+
+
+def test_beta_plus_inf_is_attention_over_pooled_keys():
+    # Nothing selected: each block contributes n_j exp(scale q.Kbar_j) and
+    # exp(scale q.Kbar_j) Vhat_j, i.e. attention over the pooled keys with an
+    # additive bias log n_j and values Vhat_j / n_j.
+    w, q, k, v = small(L=1000)
+    r = ref.solattn_head(q, k, v, math.inf, 64)
+    assert not r.sel.any()
+    nj = ref.block_sizes(w.L, 64).astype(np.float64)
+    bias = np.broadcast_to(np.log(nj)[None, :], (w.L, w.N)).copy()
+    want = sdpa(q, r.kbar, r.vhat / nj[:, None], r.scale, mask=bias)
+    np.testing.assert_allclose(r.out, want, rtol=1e-10, atol=1e-12)
+
+
+def test_exact_only_is_block_masked_attention():
+    w, q, k, v = small(L=1000)
+    r = ref.solattn_head(q, k, v, 1.0, 64)
+    out = ref.forward(q, k, v, r.sel, 64, r.scale, exact_only=True)
+    blk = np.arange(w.L) // 64
+    mask = r.sel[blk][:, blk]  # token-level: query token's block row, key token's block
+    np.testing.assert_allclose(out, sdpa(q, k, v, r.scale, mask=mask), rtol=1e-10, atol=1e-12)
+
+
+def test_hand_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+    q, k, v = (np.array(g[x], np.float64) for x in ("q", "k", "v"))
+    block, scale = g["block"], g["scale"]
+    env = {"__builtins__": {}}
+    ev = lambda s: float(eval(s, env, {"e": math.e, "inf": math.inf}))
+    for case in g["cases"]:
+        beta = ev(case["beta"])
+        r = ref.solattn_head(q, k, v, beta, block, scale=scale, exact_only=case["exact_only"])
+        np.testing.assert_allclose(r.mu, [ev(x) for x in g["mu"]], rtol=1e-14)
+        np.testing.assert_allclose(r.sigma, [ev(x) for x in g["sigma"]], rtol=1e-14)
+        if "tau" in case:
+            np.testing.assert_allclose(r.tau, [ev(x) for x in case["tau"]], rtol=1e-14)
+        np.testing.assert_array_equal(r.sel, np.array(case["selected"]))
+        want = np.array([[ev(x) for x in row] for row in case["out"]])
+        np.testing.assert_allclose(r.out, want, rtol=1e-13)
+        if not case["exact_only"]:
+            out_s, _ = ref.forward_streaming(q, k, v, r.tau, block, 1, scale)
+            np.testing.assert_allclose(out_s, want, rtol=1e-13)
+
+
+def test_executed_flops_counts():
+    # Dense selection: 4 L^2 d exact, plus the tile 2 L d N, and no approximate term.
+    L, d, b = 1000, 64, 64
+    N = ref.num_blocks(L, b)
+    sel = np.ones((N, N), bool)
+    assert ref.executed_flops(L, d, b, sel) == 4.0 * L * L * d + 2.0 * L * d * N
+    none = np.zeros((N, N), bool)
+    assert ref.executed_flops(L, d, b, none) == 2.0 * L * d * N + 2.0 * L * d * N
