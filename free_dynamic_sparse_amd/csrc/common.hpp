@@ -1,0 +1,70 @@
+// Device-side helpers shared by the Sol-Attn kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+// MI355X has 8 XCDs; consecutive workgroup ids are dealt round-robin to them.
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Map a workgroup id to a work item so that every XCD receives one
+// contiguous range of items (neighbouring query blocks of one head share
+// key/value blocks, and each XCD has its own L2).  Bijective on [0, total).
+__device__ __forceinline__ uint32_t xcd_contiguous_item(uint32_t bid, uint32_t total) {
+  const uint32_t q = total / kXcds, r = total % kXcds;
+  const uint32_t x = bid % kXcds, s = bid / kXcds;
+  return x * q + (x < r ? x : r) + s;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// 8 consecutive floats -> 8 bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* f) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)f[e];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 a, f32x4 b) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)a[e];
+    r[4 + e] = (bf16)b[e];
+  }
+  return r;
+}
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16), one wave.
+// Operand lane layout: lane l holds row (A) / column (B) l % 32 and eight
+// consecutive k values of half l / 32; result lane l holds column l % 32 and
+// rows 8*(r/4) + 4*(l/32) + r%4 for register r.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (A) / column (B) index inside a 32x32 MFMA result for register r of a
+// lane in half h.
+__device__ __forceinline__ constexpr int mfma_row(int r, int h) {
+  return 8 * (r / 4) + 4 * h + (r % 4);
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  // lanes l and l^32 hold the two halves of one 32x32 result column
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+}  // namespace solattn

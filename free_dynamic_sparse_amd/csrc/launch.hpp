@@ -1,0 +1,35 @@
+// Host-side launchers of the Sol-Attn kernels.  Arguments are already
+// validated by the C ABI layer (solattn_api.cpp) when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace solattn {
+
+struct Shape {
+  int64_t bh;     // B * H
+  int64_t L;      // tokens per head
+  int d;          // head dim (64 or 128)
+  int block;      // tokens per block (64 or 128)
+  int64_t N;      // ceil(L / block)
+  int chunk;      // pooled keys per routing chunk (1..64)
+  float beta;
+  float scale;    // softmax scale (> 0)
+  uint32_t flags;
+};
+
+hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void* v, float* qbar,
+                       float* kbar, float* vhat, hipStream_t stream);
+
+hipError_t launch_moments(const Shape& s, const float* qbar, const float* kbar, float* kmean,
+                          float* kcov, float* tau, float* mu, float* sigma, hipStream_t stream);
+
+hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                      const float* qbar, const float* kbar, const float* vhat, const float* tau,
+                      void* out, uint64_t* sel_mask, int32_t* sel_count, hipStream_t stream);
+
+hipError_t launch_dense(const Shape& s, const void* q, const void* k, const void* v, void* out,
+                        hipStream_t stream);
+
+}  // namespace solattn

@@ -1,0 +1,200 @@
+// Pooled-key moments and routing thresholds for Sol-Attn (gfx950).
+//
+// Method: "Sol-Attn: Accelerating Video Generation Inference via On-the-Fly
+// Attention Sparsification", method section, query-dependent threshold
+// routing (Eq. 4) with the row statistics obtained from the first and second
+// moments of the pooled keys (the moment identity derived in Appendix B):
+// the proxy row shat_i = scale * Qbar_i Kbar^T has mean scale * Qbar_i . m
+// and variance scale^2 * Qbar_i^T Sigma Qbar_i, so all thresholds cost
+// O(N d^2) without the N x N proxy map.
+//
+// Three small kernels, each with a fixed reduction order (deterministic):
+//   kmean_kernel   m = (1/N) sum_j Kbar_j           one workgroup per head
+//   kcov_kernel    Sigma, one 32x32 tile per workgroup, float64 sums of
+//                  centred products staged through LDS
+//   tau_kernel     mu_i, sigma_i, tau_i; each thread keeps half a row of
+//                  Sigma in registers and the workgroup walks 32 query blocks
+
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace solattn {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void kmean_kernel(const float* __restrict__ kbar,
+                                                    float* __restrict__ kmean, uint32_t N) {
+  constexpr int P = 256 / D;  // row phases
+  const int c = threadIdx.x % D;
+  const int p = threadIdx.x / D;
+  const float* src = kbar + (size_t)blockIdx.x * N * D;
+  double s = 0.0;
+  for (uint32_t j = p; j < N; j += P) s += (double)src[(size_t)j * D + c];
+  __shared__ double red[P][D];
+  red[p][c] = s;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double t = 0.0;
+#pragma unroll
+    for (int q = 0; q < P; ++q) t += red[q][c];
+    kmean[(size_t)blockIdx.x * D + c] = (float)(t / (double)N);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void kcov_kernel(const float* __restrict__ kbar,
+                                                   const float* __restrict__ kmean,
+                                                   float* __restrict__ kcov, uint32_t N) {
+  constexpr int T = D / 32;  // tiles per dimension
+  constexpr int RB = 64;     // pooled keys staged per step
+  const uint32_t bh = blockIdx.x;
+  const int r0 = 32 * (blockIdx.y / T);
+  const int c0 = 32 * (blockIdx.y % T);
+  const float* src = kbar + (size_t)bh * N * D;
+  const float* m = kmean + (size_t)bh * D;
+  __shared__ float sr[RB][33];
+  __shared__ float sc[RB][33];
+  const int ta = threadIdx.x / 16, tb = threadIdx.x % 16;
+  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+  for (uint32_t j0 = 0; j0 < N; j0 += RB) {
+    for (int e = threadIdx.x; e < RB * 32; e += 256) {
+      const int jj = e / 32, col = e % 32;
+      const uint32_t j = j0 + jj;
+      float vr = 0.f, vc = 0.f;
+      if (j < N) {
+        vr = src[(size_t)j * D + r0 + col] - m[r0 + col];
+        vc = src[(size_t)j * D + c0 + col] - m[c0 + col];
+      }
+      sr[jj][col] = vr;
+      sc[jj][col] = vc;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < RB; ++jj) {
+      const double a0 = sr[jj][2 * ta], a1 = sr[jj][2 * ta + 1];
+      const double b0 = sc[jj][2 * tb], b1 = sc[jj][2 * tb + 1];
+      acc[0][0] += a0 * b0;
+      acc[0][1] += a0 * b1;
+      acc[1][0] += a1 * b0;
+      acc[1][1] += a1 * b1;
+    }
+    __syncthreads();
+  }
+  float* dst = kcov + (size_t)bh * D * D;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+      dst[(size_t)(r0 + 2 * ta + x) * D + c0 + 2 * tb + y] = (float)(acc[x][y] / (double)N);
+}
+
+// Sum over the workgroup of one value per thread; fixed order.
+template <int NT>
+__device__ __forceinline__ float block_sum_to(float x, float* slot, int g) {
+  // wave-level butterfly, then lane 0 writes the wave total
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  if ((threadIdx.x % kWave) == 0) slot[(threadIdx.x / kWave) * 64 + g] = x;
+  return x;
+}
+
+template <int D>
+__global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qbar,
+                                                    const float* __restrict__ kmean,
+                                                    const float* __restrict__ kcov,
+                                                    float* __restrict__ tau, float* __restrict__ mu,
+                                                    float* __restrict__ sigma, uint32_t N,
+                                                    float scale, float beta) {
+  constexpr int NT = 2 * D, HALF = D / 2, G = 32, NW = NT / kWave;
+  const uint32_t bh = blockIdx.x;
+  const uint32_t i0 = blockIdx.y * G;
+  const int t = threadIdx.x, r = t / 2, h = t % 2;
+
+  // half a row of Sigma per thread, kept in registers
+  float srow[HALF];
+  const float* cov = kcov + (size_t)bh * D * D + (size_t)r * D + h * HALF;
+#pragma unroll
+  for (int e = 0; e < HALF; ++e) srow[e] = cov[e];
+
+  __shared__ float qs[G][D];
+  __shared__ float ms[D];
+  __shared__ float red_q[NW * 64];
+  __shared__ float red_m[NW * 64];
+  for (int e = t; e < G * D; e += NT) {
+    const int g = e / D, c = e % D;
+    const uint32_t i = i0 + g;
+    qs[g][c] = i < N ? qbar[((size_t)bh * N + i) * D + c] : 0.f;
+  }
+  for (int c = t; c < D; c += NT) ms[c] = kmean[(size_t)bh * D + c];
+  __syncthreads();
+
+  for (int g = 0; g < G; ++g) {
+    const float* qv = qs[g];
+    float y = 0.f;
+#pragma unroll
+    for (int e = 0; e < HALF; ++e) y = fmaf(srow[e], qv[h * HALF + e], y);
+    const float other = __shfl_xor(y, 1);
+    const float yr = (h == 0) ? (y + other) : (other + y);  // (Sigma Qbar)_r
+    const float cq = (h == 0) ? yr * qv[r] : 0.f;            // Qbar_r (Sigma Qbar)_r
+    const float cm = (h == 0) ? ms[r] * qv[r] : 0.f;         // Qbar_r m_r
+    block_sum_to<NT>(cq, red_q, g);
+    block_sum_to<NT>(cm, red_m, g);
+  }
+  __syncthreads();
+
+  if (t < G) {
+    const uint32_t i = i0 + t;
+    if (i < N) {
+      float qf = 0.f, md = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        qf += red_q[w * 64 + t];
+        md += red_m[w * 64 + t];
+      }
+      const float mu_i = scale * md;
+      const float sigma_i = sqrtf(fmaxf(scale * scale * qf, 0.f));
+      float tau_i;
+      if (beta == -INFINITY)
+        tau_i = -INFINITY;
+      else if (beta == INFINITY)
+        tau_i = INFINITY;
+      else if (sigma_i == 0.f)
+        tau_i = -INFINITY;  // constant proxy row: every block passes the >= test
+      else
+        tau_i = mu_i + beta * sigma_i;
+      const size_t o = (size_t)bh * N + i;
+      tau[o] = tau_i;
+      if (mu) mu[o] = mu_i;
+      if (sigma) sigma[o] = sigma_i;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_moments_t(const Shape& s, const float* qbar, const float* kbar, float* kmean,
+                            float* kcov, float* tau, float* mu, float* sigma, hipStream_t stream) {
+  const uint32_t bh = (uint32_t)s.bh, N = (uint32_t)s.N;
+  hipLaunchKernelGGL((kmean_kernel<D>), dim3(bh), dim3(256), 0, stream, kbar, kmean, N);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((kcov_kernel<D>), dim3(bh, (D / 32) * (D / 32)), dim3(256), 0, stream, kbar,
+                     kmean, kcov, N);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((tau_kernel<D>), dim3(bh, (N + 31) / 32), dim3(2 * D), 0, stream, qbar,
+                     kmean, kcov, tau, mu, sigma, N, s.scale, s.beta);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_moments(const Shape& s, const float* qbar, const float* kbar, float* kmean,
+                          float* kcov, float* tau, float* mu, float* sigma, hipStream_t stream) {
+  if (s.d == 128) return launch_moments_t<128>(s, qbar, kbar, kmean, kcov, tau, mu, sigma, stream);
+  if (s.d == 64) return launch_moments_t<64>(s, qbar, kbar, kmean, kcov, tau, mu, sigma, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace solattn

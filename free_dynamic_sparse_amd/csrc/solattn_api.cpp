@@ -1,0 +1,133 @@
+// C ABI of the Sol-Attn library: argument checks first, then launches.
+// Every check runs before any HIP call, so a bad argument never reaches the
+// device and the error paths can be exercised on a machine without a GPU.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/solattn.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxSeqLen = int64_t(1) << 22;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt_ptr(const void* p) { return p == nullptr || aligned16(p); }
+
+// Shape checks shared by every entry point.  Sets *empty for B*H == 0 or L == 0.
+int check_shape(const solattn_problem_t* p, solattn::Shape* s, bool* empty) {
+  if (p == nullptr) return SOLATTN_E_INVALID_ARG;
+  if (p->reserved != 0 || (p->flags & ~SOLATTN_FLAG_EXACT_ONLY) != 0) return SOLATTN_E_INVALID_ARG;
+  if (p->batch < 0 || p->heads < 0 || p->seq_len < 0 || p->seq_len > kMaxSeqLen)
+    return SOLATTN_E_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) return SOLATTN_E_UNSUPPORTED;
+  if (p->block != 64 && p->block != 128) return SOLATTN_E_UNSUPPORTED;
+  if (isnan(p->scale) || isinf(p->scale)) return SOLATTN_E_INVALID_ARG;
+  if (p->batch > 0 && p->heads > kMaxGrid / p->batch) return SOLATTN_E_INVALID_ARG;
+  const int64_t bh = p->batch * p->heads;
+  const int64_t N = (p->seq_len + p->block - 1) / p->block;
+  if (N > 0 && bh > kMaxGrid / N) return SOLATTN_E_INVALID_ARG;
+  s->bh = bh;
+  s->L = p->seq_len;
+  s->d = (int)p->head_dim;
+  s->block = p->block;
+  s->N = N;
+  s->chunk = p->chunk;
+  s->beta = p->beta;
+  s->scale = p->scale > 0.f ? p->scale : (float)(1.0 / sqrt((double)p->head_dim));
+  s->flags = p->flags;
+  *empty = (bh == 0 || N == 0);
+  return SOLATTN_OK;
+}
+
+int check_routing(const solattn_problem_t* p) {
+  if (isnan(p->beta)) return SOLATTN_E_INVALID_ARG;
+  if (p->chunk < 1 || p->chunk > 64) return SOLATTN_E_UNSUPPORTED;
+  return SOLATTN_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? SOLATTN_OK : SOLATTN_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int solattn_pool(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                 float* qbar, float* kbar, float* vhat, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(qbar) || !ok_ptr(kbar) || !ok_ptr(vhat))
+    return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_pool(s, q, k, v, qbar, kbar, vhat,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* kbar,
+                    float* kmean, float* kcov, float* tau, float* mu, float* sigma,
+                    void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (isnan(p->beta)) return SOLATTN_E_INVALID_ARG;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(qbar) || !ok_ptr(kbar) || !ok_ptr(kmean) || !ok_ptr(kcov) || !ok_ptr(tau) ||
+      !ok_opt_ptr(mu) || !ok_opt_ptr(sigma))
+    return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_moments(s, qbar, kbar, kmean, kcov, tau, mu, sigma,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                const float* qbar, const float* kbar, const float* vhat, const float* tau,
+                void* out, uint64_t* sel_mask, int32_t* sel_count, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  rc = check_routing(p);
+  if (rc != SOLATTN_OK) return rc;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(qbar) || !ok_ptr(kbar) ||
+      !ok_ptr(vhat) || !ok_ptr(tau) || !ok_ptr(out) || !ok_opt_ptr(sel_mask) ||
+      !ok_opt_ptr(sel_count))
+    return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, out, sel_mask,
+                                      sel_count, static_cast<hipStream_t>(stream)));
+}
+
+int solattn_dense_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                      void* out, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(out)) return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_dense(s, q, k, v, out, static_cast<hipStream_t>(stream)));
+}
+
+const char* solattn_strerror(int code) {
+  switch (code) {
+    case SOLATTN_OK:
+      return "ok";
+    case SOLATTN_E_INVALID_ARG:
+      return "invalid argument (null or misaligned pointer, bad shape, NaN beta or scale)";
+    case SOLATTN_E_UNSUPPORTED:
+      return "unsupported configuration (head_dim and block must be 64 or 128, chunk 1..64)";
+    case SOLATTN_E_HIP:
+      return "HIP launch failed";
+    default:
+      return "unknown error code";
+  }
+}
+
+int solattn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,220 @@
+"""Python binding of libsolattn.so (argument marshalling only).
+
+Each function below has the name of the C entry point it calls and takes
+torch tensors for the device buffers; every step of the computation runs in
+the HIP kernels behind the C ABI.  torch supplies device memory and the
+current stream.  There is no fallback: if the library is missing the import
+of this module fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libsolattn.so")
+
+SOLATTN_OK = 0
+SOLATTN_E_INVALID_ARG = -1
+SOLATTN_E_UNSUPPORTED = -2
+SOLATTN_E_HIP = -3
+SOLATTN_FLAG_EXACT_ONLY = 1
+
+EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd",
+           "solattn_strerror", "solattn_version")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of solattn_problem_t."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("seq_len", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("block", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("beta", ctypes.c_float),
+        ("scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m free_dynamic_sparse_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    pp = ctypes.POINTER(Problem)
+    lib.solattn_pool.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+    lib.solattn_moments.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.solattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.solattn_dense_fwd.argtypes = [pp, vp, vp, vp, vp, vp]
+    for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.solattn_strerror.argtypes = [ctypes.c_int]
+    lib.solattn_strerror.restype = ctypes.c_char_p
+    lib.solattn_version.argtypes = []
+    lib.solattn_version.restype = ctypes.c_int
+    return lib
+
+
+LIB = load_library()
+
+
+class SolAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {LIB.solattn_strerror(code).decode()} (code {code})")
+
+
+def problem(B: int, H: int, L: int, d: int, block: int = 128, chunk: int = 32,
+            beta: float = 1.0, scale: Optional[float] = None, exact_only: bool = False) -> Problem:
+    return Problem(B, H, L, d, block, chunk, beta, 0.0 if scale is None else scale,
+                   SOLATTN_FLAG_EXACT_ONLY if exact_only else 0, 0)
+
+
+def num_blocks(L: int, block: int) -> int:
+    return (L + block - 1) // block
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != SOLATTN_OK:
+        raise SolAttnError(rc, where)
+
+
+def _need(t: torch.Tensor, dtype, shape, name: str) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} CUDA tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()} "
+                         f"cuda={t.is_cuda}")
+
+
+def _dims(p: Problem):
+    N = num_blocks(p.seq_len, p.block)
+    return (p.batch, p.heads, p.seq_len, p.head_dim), (p.batch, p.heads, N, p.head_dim), N
+
+
+def solattn_pool(p: Problem, q, k, v, qbar, kbar, vhat, stream=None) -> None:
+    full, pooled, _ = _dims(p)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, full, n)
+    for t, n in ((qbar, "qbar"), (kbar, "kbar"), (vhat, "vhat")):
+        _need(t, torch.float32, pooled, n)
+    _check(LIB.solattn_pool(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar), _ptr(kbar),
+                            _ptr(vhat), _stream(stream)), "solattn_pool")
+
+
+def solattn_moments(p: Problem, qbar, kbar, kmean, kcov, tau, mu=None, sigma=None,
+                    stream=None) -> None:
+    _, pooled, N = _dims(p)
+    B, H, d = p.batch, p.heads, p.head_dim
+    _need(qbar, torch.float32, pooled, "qbar")
+    _need(kbar, torch.float32, pooled, "kbar")
+    _need(kmean, torch.float32, (B, H, d), "kmean")
+    _need(kcov, torch.float32, (B, H, d, d), "kcov")
+    _need(tau, torch.float32, (B, H, N), "tau")
+    for t, n in ((mu, "mu"), (sigma, "sigma")):
+        if t is not None:
+            _need(t, torch.float32, (B, H, N), n)
+    _check(LIB.solattn_moments(ctypes.byref(p), _ptr(qbar), _ptr(kbar), _ptr(kmean), _ptr(kcov),
+                               _ptr(tau), _ptr(mu), _ptr(sigma), _stream(stream)),
+           "solattn_moments")
+
+
+def solattn_fwd(p: Problem, q, k, v, qbar, kbar, vhat, tau, out, sel_mask=None, sel_count=None,
+                stream=None) -> None:
+    full, pooled, N = _dims(p)
+    B, H = p.batch, p.heads
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, full, n)
+    for t, n in ((qbar, "qbar"), (kbar, "kbar"), (vhat, "vhat")):
+        _need(t, torch.float32, pooled, n)
+    _need(tau, torch.float32, (B, H, N), "tau")
+    if sel_mask is not None:
+        _need(sel_mask, torch.int64, (B, H, N, (N + 63) // 64), "sel_mask")
+    if sel_count is not None:
+        _need(sel_count, torch.int32, (B, H, N), "sel_count")
+    _check(LIB.solattn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar), _ptr(kbar),
+                           _ptr(vhat), _ptr(tau), _ptr(out), _ptr(sel_mask), _ptr(sel_count),
+                           _stream(stream)), "solattn_fwd")
+
+
+def solattn_dense_fwd(p: Problem, q, k, v, out, stream=None) -> None:
+    full, _, _ = _dims(p)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, full, n)
+    _check(LIB.solattn_dense_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                 _stream(stream)), "solattn_dense_fwd")
+
+
+class Workspace:
+    """Device buffers for one problem shape (torch allocations)."""
+
+    def __init__(self, p: Problem, device="cuda", debug: bool = False):
+        B, H, L, d = p.batch, p.heads, p.seq_len, p.head_dim
+        N = num_blocks(L, p.block)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.qbar = torch.empty((B, H, N, d), **f32)
+        self.kbar = torch.empty((B, H, N, d), **f32)
+        self.vhat = torch.empty((B, H, N, d), **f32)
+        self.kmean = torch.empty((B, H, d), **f32)
+        self.kcov = torch.empty((B, H, d, d), **f32)
+        self.tau = torch.empty((B, H, N), **f32)
+        self.mu = torch.empty((B, H, N), **f32) if debug else None
+        self.sigma = torch.empty((B, H, N), **f32) if debug else None
+        self.sel_mask = (torch.empty((B, H, N, (N + 63) // 64), dtype=torch.int64, device=device)
+                         if debug else None)
+        self.sel_count = torch.empty((B, H, N), dtype=torch.int32, device=device) if debug else None
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0,
+            block: int = 128, chunk: int = 32, scale: Optional[float] = None,
+            exact_only: bool = False, out: Optional[torch.Tensor] = None,
+            ws: Optional[Workspace] = None, stream=None) -> torch.Tensor:
+    """The whole Sol-Attn forward: pool, moments/thresholds, fused kernel."""
+    B, H, L, d = q.shape
+    p = problem(B, H, L, d, block, chunk, beta, scale, exact_only)
+    if ws is None:
+        ws = Workspace(p, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, stream)
+    solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma, stream)
+    solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask, ws.sel_count,
+                stream)
+    return out
+
+
+def dense_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int = 128,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    B, H, L, d = q.shape
+    p = problem(B, H, L, d, block, 32, -math.inf, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    solattn_dense_fwd(p, q, k, v, out, stream)
+    return out
+
+
+def mask_to_bool(sel_mask: torch.Tensor, N: int) -> torch.Tensor:
+    """Unpack the u64 row bitmaps [..., ceil(N/64)] into bool [..., N] (CPU)."""
+    words = sel_mask.cpu().contiguous()
+    bits = torch.arange(64, dtype=torch.int64)
+    unpacked = ((words.unsqueeze(-1) >> bits) & 1).bool()
+    return unpacked.reshape(*words.shape[:-1], -1)[..., :N]

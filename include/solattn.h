@@ -1,0 +1,155 @@
+/*
+ * solattn.h - C ABI of the Sol-Attn sparse-attention forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method: "Sol-Attn: Accelerating Video Generation Inference via On-the-Fly
+ * Attention Sparsification" (arXiv 2607.24027).  One forward call is
+ *   solattn_pool     -> block proxies Qbar, Kbar and summed values Vhat
+ *   solattn_moments  -> pooled-key moments and per-query-block thresholds tau
+ *   solattn_fwd      -> the fused nested-loop attention kernel
+ * and solattn_dense_fwd is plain dense softmax attention on the same core,
+ * kept as the in-house comparison point.
+ *
+ * Conventions shared by every entry point
+ * - Tensors are contiguous row-major device memory.  Q, K, V and O are
+ *   bfloat16 [B, H, L, d]; pooled and per-block arrays are float32.
+ * - Blocks: N = ceil(L / block) query blocks and N key blocks per (b, h);
+ *   block j holds tokens [j*block, min(L, (j+1)*block)), n_j of them.
+ * - Every device pointer must be 16-byte aligned.  The caller owns every
+ *   buffer; the library never allocates, frees or synchronises.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *   stream).  All arguments are checked before any HIP call, so a bad
+ *   argument returns an error without touching the device.  A device fault
+ *   shows at the caller's next synchronisation.
+ * - B*H == 0 or L == 0 is a valid empty problem: the call returns
+ *   SOLATTN_OK and launches nothing.
+ * - Calls that write the same output buffers and overlap on one device
+ *   race; calls on distinct buffers may overlap freely.
+ */
+#ifndef SOLATTN_H_
+#define SOLATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define SOLATTN_OK 0
+#define SOLATTN_E_INVALID_ARG (-1) /* null pointer, bad shape, NaN beta, misalignment */
+#define SOLATTN_E_UNSUPPORTED (-2) /* head_dim, block or chunk outside the built set */
+#define SOLATTN_E_HIP (-3)         /* a HIP launch failed; see hipGetLastError */
+
+/* solattn_problem_t.flags */
+#define SOLATTN_FLAG_EXACT_ONLY 1u /* drop the approximation of unselected blocks */
+
+/*
+ * Problem description (host memory, read during the call only).
+ *  batch, heads, seq_len  B, H, L; each >= 0, L <= 2^22, B*H < 2^31.
+ *  head_dim               d: 64 or 128.
+ *  block                  tokens per block, 64 or 128 (the page uses square
+ *                         block x block tiles for queries and keys alike).
+ *  chunk                  C, pooled keys per routing chunk, 1..64.  C changes
+ *                         the schedule, never the result (method section,
+ *                         chunk-wise streaming thresholding).
+ *  beta                   standardized cutoff of tau_i = mu_i + beta*sigma_i
+ *                         (Eq. 4).  Any finite value; -INFINITY selects every
+ *                         block, +INFINITY none.  NaN is rejected.
+ *  scale                  softmax scale; <= 0 means 1/sqrt(head_dim).
+ *  flags                  SOLATTN_FLAG_* bits; unknown bits are rejected.
+ *  reserved               must be 0.
+ */
+typedef struct solattn_problem {
+  int64_t batch;
+  int64_t heads;
+  int64_t seq_len;
+  int64_t head_dim;
+  int32_t block;
+  int32_t chunk;
+  float beta;
+  float scale;
+  uint32_t flags;
+  uint32_t reserved;
+} solattn_problem_t;
+
+/*
+ * Block pooling (method section, block proxies of Eq. 3 and the summed
+ * values Vhat_j of Eqs. 9-10).
+ *   q, k, v  in:  bf16 [B, H, L, d]
+ *   qbar     out: f32 [B, H, N, d]  Qbar_i = mean of block i's query rows
+ *   kbar     out: f32 [B, H, N, d]  Kbar_j = mean of block j's key rows
+ *   vhat     out: f32 [B, H, N, d]  Vhat_j = sum of block j's value rows
+ * A ragged last block is pooled over its n_j valid tokens.  Accumulation is
+ * float32 in a fixed order, so results are deterministic.  Reads 3*B*H*L*d
+ * bf16 once.
+ */
+int solattn_pool(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                 float* qbar, float* kbar, float* vhat, void* stream);
+
+/*
+ * Pooled-key moments and routing thresholds (method section, query-dependent
+ * threshold routing, Eq. 4, with the moment identity of Appendix B).
+ *   qbar, kbar  in:  f32 [B, H, N, d]  from solattn_pool
+ *   kmean       out: f32 [B, H, d]     m = (1/N) sum_j Kbar_j
+ *   kcov        out: f32 [B, H, d, d]  (1/N) sum_j (Kbar_j - m)(Kbar_j - m)^T
+ *   tau         out: f32 [B, H, N]     tau_i = mu_i + beta*sigma_i
+ *   mu, sigma   out: f32 [B, H, N], each may be NULL
+ *               mu_i = scale*Qbar_i.m, sigma_i = scale*sqrt(Qbar_i^T Sigma Qbar_i):
+ *               mean and population std of the proxy row scale*Qbar_i Kbar^T,
+ *               without building the N x N map.
+ * tau_i is -INFINITY when beta is -INFINITY or sigma_i == 0 (a constant row:
+ * every block passes the >= test), +INFINITY when beta is +INFINITY.
+ * Moments accumulate in float64.
+ */
+int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* kbar,
+                    float* kmean, float* kcov, float* tau, float* mu, float* sigma,
+                    void* stream);
+
+/*
+ * The fused Sol-Attn forward (method section: chunk-wise streaming
+ * thresholding, Eqs. 6-7; zeroth-order approximation and the combined
+ * denominator and numerator, Eqs. 9-10; the token-to-block tile, Eq. 11;
+ * the nested-loop kernel of Algorithm 3.2 and Figure 4).
+ *   q, k, v    in:  bf16 [B, H, L, d]
+ *   qbar       in:  f32 [B, H, N, d]  from solattn_pool (routing scores)
+ *   kbar, vhat in:  f32 [B, H, N, d]  from solattn_pool (KC and VC chunks)
+ *   tau        in:  f32 [B, H, N]     from solattn_moments
+ *   out        out: bf16 [B, H, L, d]
+ *   sel_mask   out, may be NULL: u64 [B, H, N, ceil(N/64)]; bit (j mod 64) of
+ *              word j/64 of row (b, h, i) is set iff block j is in S_i.
+ *   sel_count  out, may be NULL: i32 [B, H, N], |S_i|.
+ * For query block i the kernel scans the pooled keys in chunks of C: the
+ * proxy score shat_ij = scale*Qbar_i.Kbar_j is compared with tau_i on chip;
+ * selected blocks get exact attention, unselected blocks the zeroth-order
+ * term (n_j * exp(centre) in the denominator, exp(centre) * Vhat_j in the
+ * numerator, centre = scale*q_r.Kbar_j), all in one online softmax.
+ * Nothing about the selection is written to memory unless sel_mask or
+ * sel_count is given.  With SOLATTN_FLAG_EXACT_ONLY unselected blocks are
+ * dropped and a row with no selected block outputs 0.
+ */
+int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                const float* qbar, const float* kbar, const float* vhat, const float* tau,
+                void* out, uint64_t* sel_mask, int32_t* sel_count, void* stream);
+
+/*
+ * Dense softmax attention softmax(scale * Q K^T) V on the same MFMA core,
+ * block by block with one online softmax (no routing).  beta, chunk and
+ * flags are ignored; block picks the tile size.
+ *   q, k, v in: bf16 [B, H, L, d];  out: bf16 [B, H, L, d]
+ */
+int solattn_dense_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                      void* out, void* stream);
+
+/* Static text for a return code. */
+const char* solattn_strerror(int code);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int solattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOLATTN_H_ */

@@ -207,7 +207,7 @@ def forward_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, kbar: np.ndarray,
     Readings: a selected block is exact only, an unselected block is
     approximate only; the ragged last block weighs n_j.  exact_only drops the
     approximate terms (plain keep-or-drop sparse attention, the page's
-    exact-only comparison).
+    exact-only comparison); a row with nothing selected then outputs 0.
     """
     L, d = q.shape
     nj = block_sizes(L, block).astype(F64)
@@ -222,7 +222,8 @@ def forward_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, kbar: np.ndarray,
     ex = scale * (qi @ np.asarray(k[keys], F64).T)          # n_i x |keys|
     ap = scale * (qi @ kbar[U].T)                           # n_i x |U|
     if ex.shape[1] + ap.shape[1] == 0:
-        raise ValueError("exact-only row with no selected block has no output")
+        # Reading: exact-only with nothing selected attends to nothing; output 0.
+        return np.zeros((b - a, d), F64)
     M = np.concatenate([ex, ap], axis=1).max(axis=1, keepdims=True)
     pe = np.exp(ex - M)
     pa = np.exp(ap - M)

@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads, exports what include/solattn.h
+declares, and rejects bad arguments before any HIP call (so these run on a
+machine without a GPU).  No compute call is made here."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "solattn.h")
+
+
+@pytest.fixture(scope="module")
+def sa():
+    from free_dynamic_sparse_amd import solattn
+    return solattn
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(solattn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd",
+                 "solattn_strerror", "solattn_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(sa):
+    for name in declared_functions():
+        assert hasattr(sa.LIB, name), name
+    assert set(declared_functions()) == set(sa.EXPORTS)
+
+
+def test_problem_struct_layout_matches_header(sa):
+    # int64 x4, int32 x2, float x2, uint32 x2 -> 56 bytes, no padding
+    assert ctypes.sizeof(sa.Problem) == 56
+    assert sa.Problem.beta.offset == 40 and sa.Problem.reserved.offset == 52
+
+
+def test_version_and_strerror(sa):
+    assert sa.LIB.solattn_version() == 100
+    for code in (0, -1, -2, -3, 7):
+        assert isinstance(sa.LIB.solattn_strerror(code), bytes)
+
+
+FAKE = 1 << 20  # a 16-byte aligned address that is never dereferenced
+
+
+def call_fwd(sa, p, ptr=FAKE, **over):
+    args = dict(q=ptr, k=ptr, v=ptr, qbar=ptr, kbar=ptr, vhat=ptr, tau=ptr, out=ptr,
+                sel_mask=None, sel_count=None)
+    args.update(over)
+    vals = [ctypes.c_void_p(args[n]) if args[n] is not None else None
+            for n in ("q", "k", "v", "qbar", "kbar", "vhat", "tau", "out", "sel_mask",
+                      "sel_count")]
+    return sa.LIB.solattn_fwd(ctypes.byref(p), *vals, None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 96, -2), ("head_dim", 256, -2), ("block", 32, -2), ("block", 256, -2),
+    ("chunk", 0, -2), ("chunk", 65, -2), ("beta", float("nan"), -1), ("scale", float("nan"), -1),
+    ("scale", float("inf"), -1), ("seq_len", -1, -1), ("batch", -2, -1), ("heads", -1, -1),
+    ("seq_len", (1 << 22) + 1, -1), ("reserved", 1, -1), ("flags", 2, -1),
+])
+def test_fwd_rejects_bad_problem(sa, field, value, code):
+    p = sa.problem(1, 2, 1000, 128, 128, 32, 1.0)
+    setattr(p, field, value)
+    assert call_fwd(sa, p) == code
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "qbar", "kbar", "vhat", "tau", "out"])
+def test_fwd_rejects_null_and_misaligned_pointers(sa, which):
+    p = sa.problem(1, 2, 1000, 128, 128, 32, 1.0)
+    assert call_fwd(sa, p, **{which: None}) == -1
+    assert call_fwd(sa, p, **{which: FAKE + 8}) == -1
+
+
+def test_fwd_rejects_misaligned_debug_outputs(sa):
+    p = sa.problem(1, 2, 1000, 128, 128, 32, 1.0)
+    assert call_fwd(sa, p, sel_mask=FAKE + 4) == -1
+    assert call_fwd(sa, p, sel_count=FAKE + 4) == -1
+
+
+def test_null_problem_is_rejected(sa):
+    nul = ctypes.POINTER(sa.Problem)()
+    assert sa.LIB.solattn_pool(nul, None, None, None, None, None, None, None) == -1
+    assert sa.LIB.solattn_moments(nul, None, None, None, None, None, None, None, None) == -1
+    assert sa.LIB.solattn_dense_fwd(nul, None, None, None, None, None) == -1
+
+
+@pytest.mark.parametrize("B,H,L", [(0, 4, 100), (2, 0, 100), (1, 1, 0)])
+def test_empty_problems_are_no_ops(sa, B, H, L):
+    p = sa.problem(B, H, L, 64, 64, 16, 1.0)
+    assert sa.LIB.solattn_pool(ctypes.byref(p), None, None, None, None, None, None, None) == 0
+    assert sa.LIB.solattn_moments(ctypes.byref(p), None, None, None, None, None, None, None,
+                                  None) == 0
+    assert call_fwd(sa, p, ptr=None) == 0
+    assert sa.LIB.solattn_dense_fwd(ctypes.byref(p), None, None, None, None, None) == 0
+
+
+def test_empty_problem_still_checks_beta_and_chunk(sa):
+    p = sa.problem(0, 4, 100, 64, 64, 16, float("nan"))
+    assert call_fwd(sa, p, ptr=None) == -1
+    p = sa.problem(0, 4, 100, 64, 64, 99, 1.0)
+    assert call_fwd(sa, p, ptr=None) == -2
+
+
+def test_grid_limit(sa):
+    # B*H*N must fit a 1-D grid (< 2^31)
+    p = sa.problem(1 << 20, 1 << 10, 4096, 64, 64, 16, 1.0)
+    assert call_fwd(sa, p) == -1
+
+
+def test_moments_and_pool_reject_bad_pointers(sa):
+    p = sa.problem(1, 1, 256, 64, 64, 16, 1.0)
+    f = ctypes.c_void_p(FAKE)
+    bad = ctypes.c_void_p(FAKE + 4)
+    assert sa.LIB.solattn_pool(ctypes.byref(p), f, f, f, f, f, bad, None) == -1
+    assert sa.LIB.solattn_moments(ctypes.byref(p), f, f, f, f, None, None, None, None) == -1
+    assert sa.LIB.solattn_moments(ctypes.byref(p), f, f, f, f, f, bad, None, None) == -1
+    p.beta = math.nan
+    assert sa.LIB.solattn_moments(ctypes.byref(p), f, f, f, f, f, None, None, None) == -1

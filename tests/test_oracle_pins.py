@@ -243,3 +243,10 @@ def test_executed_flops_counts():
     assert ref.executed_flops(L, d, b, sel) == 4.0 * L * L * d + 2.0 * L * d * N
     none = np.zeros((N, N), bool)
     assert ref.executed_flops(L, d, b, none) == 2.0 * L * d * N + 2.0 * L * d * N
+
+
+def test_exact_only_with_nothing_selected_outputs_zero():
+    w, q, k, v = small(L=200)
+    r = ref.solattn_head(q, k, v, math.inf, 64, exact_only=True)
+    assert not r.sel.any()
+    assert np.all(r.out == 0.0)
