@@ -69,7 +69,7 @@ struct AttnArgs {
   int32_t* sel_count;
   int64_t L;
   uint32_t N;
-  uint32_t items;
+  uint32_t per_xcd;  // query blocks per XCD slab: ceil(N / 8)
   int chunk;
   float scale;
   float c_log2;  // scale * log2(e): logits enter exp2 in this unit
@@ -351,9 +351,9 @@ __global__ __launch_bounds__(2 * BLK) void attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int h = lane / 32, l32 = lane % 32;
-  const uint32_t item = xcd_contiguous_item(blockIdx.x, a.items);  // (b*H + h)*N + i
-  const uint32_t bh = item / a.N;
-  const uint32_t i = item - bh * a.N;
+  uint32_t bh, i;
+  if (!head_striped_item(blockIdx.x, a.N, a.per_xcd, &bh, &i)) return;
+  const uint32_t item = bh * a.N + i;  // (b*H + h)*N + i
   const int64_t L = a.L;
   const int n_i = (int)((L - (int64_t)i * BLK) < BLK ? (L - (int64_t)i * BLK) : BLK);
   const int n_last = (int)(L - (int64_t)(a.N - 1) * BLK);
@@ -473,13 +473,13 @@ __global__ __launch_bounds__(2 * BLK) void attn_kernel(AttnArgs a) {
 
 template <bool FUSED>
 hipError_t launch_attn(const Shape& s, AttnArgs a, hipStream_t stream) {
-  a.items = (uint32_t)(s.bh * s.N);
   a.L = s.L;
   a.N = (uint32_t)s.N;
+  a.per_xcd = (uint32_t)((s.N + kXcds - 1) / kXcds);
   a.chunk = s.chunk;
   a.scale = s.scale;
   a.c_log2 = s.scale * kLog2e;
-  const dim3 grid(a.items);
+  const dim3 grid((uint32_t)(kXcds * a.per_xcd * s.bh));
 #define SOLATTN_LAUNCH(DD, BB)                                                              \
   if (s.d == DD && s.block == BB) {                                                         \
     hipLaunchKernelGGL((attn_kernel<DD, BB, FUSED>), grid, dim3(Cfg<DD, BB>::NT), 0, stream, \

@@ -29,7 +29,8 @@ int check_shape(const solattn_problem_t* p, solattn::Shape* s, bool* empty) {
   if (p->batch > 0 && p->heads > kMaxGrid / p->batch) return SOLATTN_E_INVALID_ARG;
   const int64_t bh = p->batch * p->heads;
   const int64_t N = (p->seq_len + p->block - 1) / p->block;
-  if (N > 0 && bh > kMaxGrid / N) return SOLATTN_E_INVALID_ARG;
+  // the attention grid holds 8 * ceil(N / 8) workgroups per (b, h)
+  if (N > 0 && bh > kMaxGrid / (N + 8)) return SOLATTN_E_INVALID_ARG;
   s->bh = bh;
   s->L = p->seq_len;
   s->d = (int)p->head_dim;
