@@ -9,11 +9,30 @@
 // Work decomposition.  One workgroup serves a pair of neighbouring query
 // blocks (2p, 2p+1) of one head: waves [0, QW) own block 2p, waves [QW, 2QW)
 // own block 2p+1, one wave per 32 query rows.  Each group keeps its own
-// routing threshold, selected set and online-softmax state.  Neighbouring
-// blocks select nearly the same key blocks, so a key block in either set is
-// loaded into LDS once and consumed by whichever group selected it; the two
-// groups also put two waves on every SIMD, so one group's softmax (VALU)
-// overlaps the other's MFMA work.
+// threshold, selected set and online-softmax state.  Neighbouring blocks
+// select nearly the same key blocks, so a key block in either set is loaded
+// into LDS once and used by whichever group selected it; the two groups also
+// put two waves on every SIMD, so one wave's softmax (VALU) can overlap the
+// other's MFMA work.
+//
+// The nested loop of Algorithm 3.2, pipelined for latency:
+//   * outer loop (routing and approximation), run over all chunks first:
+//     the chunk's pooled keys Kbar_j and summed values Vhat_j are staged in
+//     LDS; every wave computes shat_ij = scale * Qbar_i . Kbar_j in float32
+//     for both groups and ballots shat_ij >= tau_i (the same instructions on
+//     the same data in every wave, so the masks agree without communication;
+//     the page reads these scores off the token-to-block tile as column
+//     means, the same number, which a bf16 tile could not resolve inside the
+//     tie band); the selected bits go to an on-chip bitmap; the unselected
+//     columns of the token-to-block tile scale * Q_i KC^T (MFMA, KC in bf16)
+//     update the group's online softmax with weight n_j and value Vhat_j.
+//   * inner loops (exact attention), then run back to back over the selected
+//     blocks of all chunks in order, so that the next block's K/V are always
+//     in flight: K and V are double-buffered in LDS, loaded with direct-to-LDS
+//     loads (global_load_lds_dwordx4, 1 KB per wave instruction) into
+//     XOR-swizzled tiles, one workgroup barrier per key block.
+// Exact and approximate terms share one running max, denominator and
+// accumulator; the order in which they enter is immaterial to the result.
 //
 // MFMA layout (v_mfma_f32_32x32x16_bf16), computed transposed so each lane
 // owns one query:
@@ -22,25 +41,8 @@
 //                    the softmax row max / sum is lane-local plus one
 //                    exchange with lane l^32;
 //   O^T += V^T P^T   A = V^T via the LDS transpose read (ds_read_b64_tr_b16)
-//                    of row-major V, B = P^T straight from the S^T registers.
-// K and V blocks travel global -> LDS with direct-to-LDS loads
-// (global_load_lds_dwordx4, 1 KB per wave instruction) into XOR-swizzled
-// tiles; the next selected block's K is fetched while this block's softmax
-// and P V run, its V while the next S^T is computed.
-//
-// Outer loop, per chunk of C pooled keys (staged 32 at a time as float32):
-//   * routing: every wave computes shat_ij = scale * Qbar_i . Kbar_j in
-//     float32 for both groups and ballots shat_ij >= tau_i.  Every wave runs
-//     the same instructions on the same data, so the masks agree across the
-//     workgroup without communication.  (The page reads these scores off the
-//     token-to-block tile as column means; the mean is the same number, and
-//     the direct float32 dot keeps the decision far inside the tie band that
-//     a bf16 tile would not.)
-//   * approximation: the token-to-block tile scale * Q_i KC^T on MFMA (KC
-//     rounded to bf16); each group's unselected columns update its online
-//     softmax with weight n_j and value Vhat_j (VC).
-// Inner loop: the chunk's selected key blocks, exact attention.  Exact and
-// approximate terms share one running max, denominator and accumulator.
+//                    of row-major V, B = P^T packed to bf16 straight from
+//                    the S^T result registers.
 
 #include <math.h>
 
@@ -53,6 +55,9 @@ namespace {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Largest number of blocks per head the fused kernel keeps selection bits for.
+constexpr int kMaxBlocks = 8192;
 
 template <int D, int BLK>
 struct Cfg {
@@ -69,18 +74,23 @@ struct Cfg {
   static constexpr int DMA = TILE / 1024 / WAVES;  // 1 KB loads per wave per tile
   static constexpr int ROWS_1K = 1024 / ROW;       // tile rows per 1 KB load
   static constexpr int SUB = 32;            // pooled rows staged at a time
-  static constexpr int CROW = 4 * D + 16;   // bytes per float32 pooled row (16 B pad)
+  static constexpr int PROW = 4 * D;        // bytes per float32 pooled row
+  static constexpr int PSEGS = D / 4;       // 16-byte segments in a pooled row
   static_assert(DMA * WAVES * 1024 == TILE, "tile must split into whole 1 KB loads");
+  static_assert(SUB * PROW <= TILE, "a staged sub-chunk must fit one tile buffer");
 };
 
-// XOR swizzles of the 16-byte segments of tile row r (no padding possible
-// with lane-linear direct-to-LDS writes).  K: the A-operand reads of 16
-// consecutive rows hit 16 distinct segments.  V: each transpose read covers
-// 8 rows x 64 bytes; rows r..r+3 land in disjoint 64-byte bank ranges.
+// XOR swizzles of 16-byte segments (rows are written lane-linearly by the
+// direct-to-LDS loads, so padding is not available).  K: the A-operand
+// reads of 16 consecutive rows hit 16 distinct segments.  V: each transpose
+// read covers 8 rows x 64 bytes; rows r..r+3 land in disjoint 64-byte bank
+// ranges.  Pooled rows: the 32 routing lanes read 32 distinct segments.
 template <int SEGS>
 __device__ __forceinline__ int swz_k(int r) { return r % SEGS; }
 template <int SEGS>
 __device__ __forceinline__ int swz_v(int r) { return (4 * (r % 4)) % SEGS; }
+template <int PSEGS>
+__device__ __forceinline__ int swz_p(int r) { return r % PSEGS; }
 
 struct AttnArgs {
   const uint16_t* q;
@@ -116,6 +126,42 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The running max is only raised when a score exceeds it by more than
+// 2^kLazyRescale (log2 units); below that, probabilities up to 2^8 simply
+// enter the float32 sums and the bf16 P operand and the O^T rescale is
+// skipped.  Normalising by the same denominator keeps the result exact.
+constexpr float kLazyRescale = 8.f;
+
+template <int DT>
+__device__ __forceinline__ void raise_max(float mx, float& m_run, float& l_run, f32x16* o) {
+  if (__ballot(mx > m_run + kLazyRescale)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+  }
+}
+
+// Sum of the eight bf16 values of p (two per v_dot2_f32_bf16) added to acc.
+__device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 one;
+  one[0] = (bf16)1.f;
+  one[1] = (bf16)1.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    bf16x2 pr;
+    pr[0] = p[e];
+    pr[1] = p[e + 1];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------- exact path
+
 // Issue this wave's share of the direct-to-LDS loads of one K or V tile.
 // Rows >= nkeys re-read row nkeys-1 (finite data that the softmax masks).
 template <int D, int BLK, bool IS_V>
@@ -134,12 +180,24 @@ __device__ __forceinline__ void dma_tile(char* tile, const uint16_t* gblk, int n
   }
 }
 
-// S^T (keys x this wave's 32 queries) = K Q^T for the key tile in LDS.
 template <int D, int BLK>
-__device__ __forceinline__ void qk_tile(const char* ktile, const bf16x8* qreg, f32x16* s,
-                                        int lane) {
+__device__ __forceinline__ void dma_block(char* ktile, char* vtile, const uint16_t* kh,
+                                          const uint16_t* vh, uint32_t j, int nkeys, int wave,
+                                          int lane) {
+  dma_tile<D, BLK, false>(ktile, kh + (size_t)j * BLK * D, nkeys, wave, lane);
+  dma_tile<D, BLK, true>(vtile, vh + (size_t)j * BLK * D, nkeys, wave, lane);
+}
+
+// One key block of exact attention for this wave's 32 queries: S^T = K Q^T,
+// online-softmax update, O^T += V^T P^T.  The exponentials of P V k-step
+// kk + 1 are independent of the MFMAs of step kk, so the two overlap.
+template <int D, int BLK>
+__device__ __forceinline__ void exact_block(const char* ktile, const char* vtile,
+                                            const bf16x8* qreg, int nkeys, float c,
+                                            float& m_run, float& l_run, f32x16* o, int lane) {
   using C = Cfg<D, BLK>;
   const int h = lane / 32, l32 = lane % 32;
+  f32x16 s[C::MT];
 #pragma unroll
   for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
@@ -153,24 +211,14 @@ __device__ __forceinline__ void qk_tile(const char* ktile, const bf16x8* qreg, f
       const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ktile + row * C::ROW + seg * 16);
       s[mt] = mfma32x32x16(ka, qreg[ks], s[mt]);
     }
-    // keep at most one k-step of operands in flight (register budget)
-    __builtin_amdgcn_sched_barrier(0);
   }
-}
-
-// Online-softmax update with the exact scores of one key block (nkeys valid
-// keys); leaves P^T (unnormalised, float) in s.
-template <int D, int BLK>
-__device__ __forceinline__ void softmax_block(f32x16* s, int nkeys, float c, float& m_run,
-                                              float& l_run, f32x16* o, int lane) {
-  using C = Cfg<D, BLK>;
-  const int h = lane / 32;
   if (nkeys < BLK) {
+    const int lim = nkeys - 4 * h;  // key 32mt + 8(r/4) + 4h + r%4 is valid iff < nkeys
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (32 * mt + mfma_row(r, h) >= nkeys) s[mt][r] = -INFINITY;
+        if (32 * mt + 8 * (r / 4) + (r % 4) >= lim) s[mt][r] = -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -178,37 +226,17 @@ __device__ __forceinline__ void softmax_block(f32x16* s, int nkeys, float c, flo
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
   mx = wave_max_pair(mx);
-  const float m_new = fmaxf(m_run, mx * c);
-  const float alpha = fast_exp2(m_run - m_new);
+  raise_max<C::DT>(mx * c, m_run, l_run, o);
   float psum = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(__builtin_fmaf(s[mt][r], c, -m_new));
-      s[mt][r] = p;
-      psum += p;
-    }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-  if (__ballot(alpha != 1.f)) {
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
-  }
-}
-
-// O^T += V^T P^T for the value tile in LDS.
-template <int D, int BLK>
-__device__ __forceinline__ void pv_tile(const char* vtile, const f32x16* s, f32x16* o, int lane) {
-  using C = Cfg<D, BLK>;
   const int g = lane / 16, j = lane % 16;
 #pragma unroll
   for (int kk = 0; kk < C::PK; ++kk) {
     const int mt = kk / 2, hf = kk % 2;
     float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = s[mt][8 * hf + e];
-    const bf16x8 pb = pack_bf16x8(pv);
+    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[mt][8 * hf + e], c, -m_run));
+    const bf16x8 pk = pack_bf16x8(pv);
+    psum = sum_bf16x8(pk, psum);
     const int row = 16 * kk + 4 * (g / 2) + j / 4;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
@@ -219,60 +247,141 @@ __device__ __forceinline__ void pv_tile(const char* vtile, const f32x16* s, f32x
       const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0));
       const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0 + 8 * C::ROW));
       const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb, o[dt]);
+      o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pk, o[dt]);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
+  l_run += psum;
 }
 
-// Copy pooled rows [j0, j0 + rows) of Kbar and Vhat (float32) to LDS; the
-// rest of the SUB staged rows are zero so readers need no bounds checks.
+// Iterates, in increasing order, over the blocks whose bit is set in the
+// union of the two groups' bitmaps (wave-uniform state).
+struct BlockWalker {
+  const uint32_t* b0;
+  const uint32_t* b1;
+  uint32_t words;  // 32-bit words in each bitmap
+  uint32_t w;      // current word
+  uint32_t rem;    // bits of word w not yet returned
+  __device__ __forceinline__ bool next(uint32_t* j) {
+    while (rem == 0) {
+      if (++w >= words) return false;
+      rem = __builtin_amdgcn_readfirstlane(b0[w] | b1[w]);
+    }
+    const uint32_t bit = (uint32_t)__builtin_ctz(rem);
+    rem &= rem - 1;
+    *j = 32 * w + bit;
+    return true;
+  }
+};
+
+// Exact attention over every block of the union bitmap (or all N blocks
+// when `bits` is null: the dense kernel), double-buffered.  Group grp takes
+// the blocks whose bit is set in its own bitmap.
 template <int D, int BLK>
-__device__ __forceinline__ void stage_pooled(char* kch, char* vch, const float* kbar_h,
+__device__ __forceinline__ void exact_phase(char* k0, char* v0, char* k1, char* v1,
+                                            const uint32_t (*bits)[kMaxBlocks / 32],
+                                            uint32_t N, int64_t L, const uint16_t* kh,
+                                            const uint16_t* vh, bool grp_on, int grp,
+                                            const bf16x8* qreg, float c, float& m_run,
+                                            float& l_run, f32x16* o, int wave, int lane) {
+  auto nkeys_of = [&](uint32_t j) {
+    const int64_t rem = L - (int64_t)j * BLK;
+    return (int)(rem < BLK ? rem : BLK);
+  };
+  auto active_for = [&](uint32_t j) {
+    if (!grp_on) return false;
+    if (bits == nullptr) return true;
+    return ((bits[grp][j / 32] >> (j % 32)) & 1u) != 0u;
+  };
+  // dense: all blocks in order; fused: the union bitmap
+  uint32_t dense_next = 0;
+  BlockWalker wk{bits ? bits[0] : nullptr, bits ? bits[1] : nullptr, (N + 31) / 32, 0u, 0u};
+  if (bits) wk.rem = __builtin_amdgcn_readfirstlane(bits[0][0] | bits[1][0]);
+  auto next = [&](uint32_t* j) {
+    if (bits) return wk.next(j);
+    if (dense_next >= N) return false;
+    *j = dense_next++;
+    return true;
+  };
+  uint32_t j;
+  if (!next(&j)) return;
+  dma_block<D, BLK>(k0, v0, kh, vh, j, nkeys_of(j), wave, lane);
+  while (true) {
+    // even step: compute from buffer 0, prefetch into buffer 1
+    uint32_t jn;
+    bool more = next(&jn);
+    wait_vm<0>();
+    barrier_lds();  // block j is in buffer 0; everyone is done with buffer 1
+    if (more) dma_block<D, BLK>(k1, v1, kh, vh, jn, nkeys_of(jn), wave, lane);
+    if (active_for(j)) exact_block<D, BLK>(k0, v0, qreg, nkeys_of(j), c, m_run, l_run, o, lane);
+    if (!more) break;
+    j = jn;
+    // odd step: compute from buffer 1, prefetch into buffer 0
+    more = next(&jn);
+    wait_vm<0>();
+    barrier_lds();
+    if (more) dma_block<D, BLK>(k0, v0, kh, vh, jn, nkeys_of(jn), wave, lane);
+    if (active_for(j)) exact_block<D, BLK>(k1, v1, qreg, nkeys_of(j), c, m_run, l_run, o, lane);
+    if (!more) break;
+    j = jn;
+  }
+  barrier_lds();  // buffers free for whoever comes next
+}
+
+// ---------------------------------------------------------- routing / approx
+
+// Stage pooled rows [j0, j0 + rows) of Kbar into kst and Vhat into vst
+// (float32, swizzled 16-byte segments); the rest of the SUB rows are zero so
+// readers need no bounds checks.
+template <int D, int BLK>
+__device__ __forceinline__ void stage_pooled(char* kst, char* vst, const float* kbar_h,
                                              const float* vhat_h, uint32_t j0, int rows,
                                              int tid) {
   using C = Cfg<D, BLK>;
-  constexpr int P = D / 4;  // 16-byte pieces per row
-  constexpr int IT = (C::SUB * P + C::NT - 1) / C::NT;
+  constexpr int IT = (C::SUB * C::PSEGS + C::NT - 1) / C::NT;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = tid + it * C::NT;
-    const int jj = idx / P, pc = idx % P;
+    const int jj = idx / C::PSEGS, sg = idx % C::PSEGS;
     if (jj < C::SUB) {
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if (jj < rows) {
-        const size_t gofs = (size_t)(j0 + jj) * D + pc * 4;
+        const size_t gofs = (size_t)(j0 + jj) * D + sg * 4;
         kk = *reinterpret_cast<const f32x4*>(kbar_h + gofs);
         vv = *reinterpret_cast<const f32x4*>(vhat_h + gofs);
       }
-      *reinterpret_cast<f32x4*>(kch + jj * C::CROW + pc * 16) = kk;
-      *reinterpret_cast<f32x4*>(vch + jj * C::CROW + pc * 16) = vv;
+      const int at = jj * C::PROW + (sg ^ swz_p<C::PSEGS>(jj)) * 16;
+      *reinterpret_cast<f32x4*>(kst + at) = kk;
+      *reinterpret_cast<f32x4*>(vst + at) = vv;
     }
   }
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ const float* pooled_at(const char* st, int row, int col) {
+  using C = Cfg<D, BLK>;
+  return reinterpret_cast<const float*>(st + row * C::PROW +
+                                        ((col / 4) ^ swz_p<C::PSEGS>(row)) * 16) +
+         (col % 4);
 }
 
 // Routing of up to 32 staged pooled keys for both query blocks of the pair:
 // bit jj of mask g is set iff pooled key jj (< rows) has shat >= tau_g.
 template <int D, int BLK>
-__device__ __forceinline__ void route_sub(const char* kch, const float (*qbar_s)[D], int rows,
+__device__ __forceinline__ void route_sub(const char* kst, const float (*qbar_s)[D], int rows,
                                           float tau0, float tau1, float scale, int lane,
                                           uint32_t* m0, uint32_t* m1) {
-  using C = Cfg<D, BLK>;
   constexpr int HALF = D / 2;
   const int h = lane / 32, jj = lane % 32;
   float p0 = 0.f, p1 = 0.f;
-  if (jj < rows) {
-    const float* kr = reinterpret_cast<const float*>(kch + jj * C::CROW) + h * HALF;
 #pragma unroll
-    for (int e = 0; e < HALF; e += 4) {
-      const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + e);
-      const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][h * HALF + e]);
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][h * HALF + e]);
+  for (int e = 0; e < HALF; e += 4) {
+    const f32x4 kv = *reinterpret_cast<const f32x4*>(pooled_at<D, BLK>(kst, jj, h * HALF + e));
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][h * HALF + e]);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][h * HALF + e]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        p0 = __builtin_fmaf(q0[x], kv[x], p0);
-        p1 = __builtin_fmaf(q1[x], kv[x], p1);
-      }
+    for (int x = 0; x < 4; ++x) {
+      p0 = __builtin_fmaf(q0[x], kv[x], p0);
+      p1 = __builtin_fmaf(q1[x], kv[x], p1);
     }
   }
   const float o0 = __shfl_xor(p0, 32), o1 = __shfl_xor(p1, 32);
@@ -286,7 +395,7 @@ __device__ __forceinline__ void route_sub(const char* kch, const float (*qbar_s)
 // (Eqs. 9-10): logits from the token-to-block tile, weight n_j in the
 // denominator, Vhat_j in the numerator.  jbase = index of staged row 0.
 template <int D, int BLK>
-__device__ __forceinline__ void approx_sub(const char* kch, const char* vch, const bf16x8* qreg,
+__device__ __forceinline__ void approx_sub(const char* kst, const char* vst, const bf16x8* qreg,
                                            uint32_t unsel, uint32_t jbase, uint32_t N,
                                            int n_last, float c, float& m_run, float& l_run,
                                            f32x16* o, int lane) {
@@ -298,10 +407,10 @@ __device__ __forceinline__ void approx_sub(const char* kch, const char* vch, con
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     // staged row l32 (finite; zero past the staged rows) feeds this lane's A operand
-    const float* src = reinterpret_cast<const float*>(kch + l32 * C::CROW) + 16 * ks + 8 * h;
-    const bf16x8 ka = pack_bf16x8(*reinterpret_cast<const f32x4*>(src),
-                                  *reinterpret_cast<const f32x4*>(src + 4));
-    t = mfma32x32x16(ka, qreg[ks], t);
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(pooled_at<D, BLK>(kst, l32, 16 * ks + 8 * h));
+    const f32x4 a1 =
+        *reinterpret_cast<const f32x4*>(pooled_at<D, BLK>(kst, l32, 16 * ks + 8 * h + 4));
+    t = mfma32x32x16(pack_bf16x8(a0, a1), qreg[ks], t);
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -310,95 +419,43 @@ __device__ __forceinline__ void approx_sub(const char* kch, const char* vch, con
     mx = fmaxf(mx, t[r]);
   }
   mx = wave_max_pair(mx);
-  const float m_new = fmaxf(m_run, mx * c);
-  const float alpha = fast_exp2(m_run - m_new);
+  raise_max<C::DT>(mx * c, m_run, l_run, o);
   float lsum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float p = fast_exp2(__builtin_fmaf(t[r], c, -m_new));
-    t[r] = p;
-    const float w = (jbase + mfma_row(r, h) == N - 1) ? (float)n_last : (float)BLK;
-    lsum = __builtin_fmaf(w, p, lsum);
-  }
-  l_run = l_run * alpha + lsum;
-  m_run = m_new;
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = t[8 * hf + e];
-    const bf16x8 pb = pack_bf16x8(pv);
+    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(t[8 * hf + e], c, -m_run));
+    const bf16x8 pk = pack_bf16x8(pv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // weight n_j of the block behind pooled key jbase + row (bf16 P, as the numerator)
+      const float w = (jbase + mfma_row(8 * hf + e, h) == N - 1) ? (float)n_last : (float)BLK;
+      lsum = __builtin_fmaf(w, (float)pk[e], lsum);
+    }
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       float vv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // columns outside unsel carry p = 0 against finite staged values
-        const int jr = mfma_row(8 * hf + e, h);
-        vv[e] = reinterpret_cast<const float*>(vch + jr * C::CROW)[32 * dt + l32];
-      }
-      o[dt] = mfma32x32x16(pack_bf16x8(vv), pb, o[dt]);
+      for (int e = 0; e < 8; ++e)  // columns outside unsel carry p = 0 against finite values
+        vv[e] = *pooled_at<D, BLK>(vst, mfma_row(8 * hf + e, h), 32 * dt + l32);
+      o[dt] = mfma32x32x16(pack_bf16x8(vv), pk, o[dt]);
     }
   }
+  l_run += lsum;
 }
 
-// Exact attention over the key blocks j0 + bit of `both` (in increasing
-// order); this wave's group takes the blocks whose bit is set in `mine`.
-// K/V of the next block are prefetched while the current one is consumed.
-template <int D, int BLK>
-__device__ __forceinline__ void exact_blocks(char* ktile, char* vtile, const uint16_t* kh,
-                                             const uint16_t* vh, int64_t L, uint32_t j0,
-                                             uint64_t both, uint64_t mine, const bf16x8* qreg,
-                                             float c, float& m_run, float& l_run, f32x16* o,
-                                             int wave, int lane) {
-  using C = Cfg<D, BLK>;
-  if (both == 0) return;
-  auto nkeys_of = [&](uint32_t j) {
-    const int64_t rem = L - (int64_t)j * BLK;
-    return (int)(rem < BLK ? rem : BLK);
-  };
-  wait_vm<0>();
-  uint32_t j = j0 + (uint32_t)__builtin_ctzll(both);
-  both &= both - 1;
-  dma_tile<D, BLK, false>(ktile, kh + (size_t)j * BLK * D, nkeys_of(j), wave, lane);
-  dma_tile<D, BLK, true>(vtile, vh + (size_t)j * BLK * D, nkeys_of(j), wave, lane);
-  f32x16 s[C::MT];
-  while (true) {
-    const bool has_next = both != 0;
-    const uint32_t jn = has_next ? j0 + (uint32_t)__builtin_ctzll(both) : 0u;
-    const bool active = (mine >> (j - j0)) & 1ull;
-    const int nk = nkeys_of(j);
-    wait_vm<C::DMA>();  // this block's K has landed (its V may still be in flight)
-    barrier_lds();
-    if (active) qk_tile<D, BLK>(ktile, qreg, s, lane);
-    barrier_lds();      // every wave is done with K
-    if (has_next)
-      dma_tile<D, BLK, false>(ktile, kh + (size_t)jn * BLK * D, nkeys_of(jn), wave, lane);
-    if (active) softmax_block<D, BLK>(s, nk, c, m_run, l_run, o, lane);
-    if (has_next)
-      wait_vm<C::DMA>();  // V has landed (the next K may still be in flight)
-    else
-      wait_vm<0>();
-    barrier_lds();
-    if (active) pv_tile<D, BLK>(vtile, s, o, lane);
-    barrier_lds();      // every wave is done with V
-    if (!has_next) break;
-    dma_tile<D, BLK, true>(vtile, vh + (size_t)jn * BLK * D, nkeys_of(jn), wave, lane);
-    j = jn;
-    both &= both - 1;
-  }
-}
+// ------------------------------------------------------------------ kernel
 
 template <int D, int BLK, bool FUSED>
 __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) char ktile[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char vtile[C::TILE];
-  __shared__ __attribute__((aligned(16))) char kch[FUSED ? C::SUB * C::CROW : 16];
-  __shared__ __attribute__((aligned(16))) char vch[FUSED ? C::SUB * C::CROW : 16];
-  __shared__ __attribute__((aligned(16))) float qbar_s[2][D];
+  __shared__ __attribute__((aligned(1024))) char k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v1[C::TILE];
+  __shared__ uint32_t selbits[FUSED ? 2 : 1][FUSED ? kMaxBlocks / 32 : 1];
+  __shared__ __attribute__((aligned(16))) float qbar_s[FUSED ? 2 : 1][D];
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int grp = wave / C::QW;  // which block of the pair
@@ -406,13 +463,12 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   uint32_t bh, pair;
   if (!head_striped_item(blockIdx.x, a.pairs, a.per_xcd, &bh, &pair)) return;
   const uint32_t N = a.N;
-  const uint32_t i_g = 2 * pair + grp;       // this group's query block
-  const bool grp_on = i_g < N;               // block 2p+1 may not exist
+  const uint32_t i_g = 2 * pair + grp;  // this group's query block
+  const bool grp_on = i_g < N;          // block 2p+1 may not exist
   const bool pair1_on = 2 * pair + 1 < N;
   const int64_t L = a.L;
   const int n_i =
       grp_on ? (int)((L - (int64_t)i_g * BLK) < BLK ? (L - (int64_t)i_g * BLK) : BLK) : 0;
-  const int n_last = (int)(L - (int64_t)(N - 1) * BLK);
   const size_t head = (size_t)bh * (size_t)L * D;
   const uint16_t* qh = a.q + head;
   const uint16_t* kh = a.k + head;
@@ -437,74 +493,75 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
   if constexpr (FUSED) {
+    // ---- outer loop: routing and approximation over every chunk
     const uint32_t item0 = bh * N + 2 * pair;
     const float tau0 = a.tau[item0];
     const float tau1 = pair1_on ? a.tau[item0 + 1] : INFINITY;
     for (int cc = tid; cc < 2 * D; cc += C::NT) {
-      const int g = cc / D;
-      qbar_s[g][cc % D] = (g == 0 || pair1_on) ? a.qbar[(size_t)(item0 + g) * D + cc % D] : 0.f;
+      const int gq = cc / D;
+      qbar_s[gq][cc % D] =
+          (gq == 0 || pair1_on) ? a.qbar[(size_t)(item0 + gq) * D + cc % D] : 0.f;
     }
+    const uint32_t words = (N + 31) / 32;
+    for (uint32_t w = tid; w < 2 * words; w += C::NT) selbits[w / words][w % words] = 0u;
     const float* kbar_h = a.kbar + (size_t)bh * N * D;
     const float* vhat_h = a.vhat + (size_t)bh * N * D;
+    const int n_last = (int)(L - (int64_t)(N - 1) * BLK);
     const uint32_t chunk = (uint32_t)a.chunk;
-    const uint32_t T = (N + chunk - 1) / chunk;
-    const uint32_t W = (N + 63) / 64;
-    // the group's first wave keeps the debug bitmap (wave-uniform); lane 0 stores
-    const bool writer = grp_on && (wave % C::QW) == 0;
-    uint64_t* mrow = (a.sel_mask && writer) ? a.sel_mask + (size_t)(bh * N + i_g) * W : nullptr;
-    uint32_t cur_word = 0;
-    uint64_t cur_bits = 0;
-    int count = 0;
-    for (uint32_t t = 0; t < T; ++t) {
-      const uint32_t j0 = t * chunk;
+    for (uint32_t j0 = 0; j0 < N; j0 += chunk) {
       const int cvalid = (int)((N - j0) < chunk ? (N - j0) : chunk);
-      uint64_t mask0 = 0, mask1 = 0;
       for (int sb = 0; sb < cvalid; sb += C::SUB) {
         const int rows = (cvalid - sb) < C::SUB ? (cvalid - sb) : C::SUB;
+        const uint32_t jb = j0 + sb;  // pooled key of staged row 0
         __syncthreads();  // previous readers of the staging buffers are done
-        stage_pooled<D, BLK>(kch, vch, kbar_h, vhat_h, j0 + sb, rows, tid);
+        stage_pooled<D, BLK>(k1, v1, kbar_h, vhat_h, jb, rows, tid);
         __syncthreads();
         uint32_t s0, s1;
-        route_sub<D, BLK>(kch, qbar_s, rows, tau0, tau1, a.scale, lane, &s0, &s1);
-        mask0 |= (uint64_t)s0 << sb;
-        mask1 |= (uint64_t)s1 << sb;
-        const uint32_t mine_s = grp == 0 ? s0 : s1;
+        route_sub<D, BLK>(k1, qbar_s, rows, tau0, tau1, a.scale, lane, &s0, &s1);
+        if (!pair1_on) s1 = 0u;
+        if (tid == 0) {  // append to the bitmaps (single writer, in order)
+          const uint32_t wd = jb / 32, sh = jb % 32;
+          selbits[0][wd] |= s0 << sh;
+          selbits[1][wd] |= s1 << sh;
+          if (sh != 0 && sh + (uint32_t)rows > 32) {
+            selbits[0][wd + 1] |= s0 >> (32 - sh);
+            selbits[1][wd + 1] |= s1 >> (32 - sh);
+          }
+        }
+        const uint32_t mine = grp == 0 ? s0 : s1;
         const uint32_t valid = rows >= 32 ? 0xffffffffu : ((1u << rows) - 1u);
-        const uint32_t unsel = valid & ~mine_s;
+        const uint32_t unsel = valid & ~mine;
         if (grp_on && !a.exact_only && unsel)
-          approx_sub<D, BLK>(kch, vch, qreg, unsel, j0 + sb, N, n_last, a.c_log2, m_run, l_run,
-                             o, lane);
+          approx_sub<D, BLK>(k1, v1, qreg, unsel, jb, N, n_last, a.c_log2, m_run, l_run, o,
+                             lane);
       }
-      if (!pair1_on) mask1 = 0;
-      const uint64_t mine = grp == 0 ? mask0 : mask1;
-      if (mrow) {
-        // append this chunk's bits to the row bitmap (chunks arrive in order)
-        const uint32_t word = j0 / 64, sh = j0 % 64;
-        if (word != cur_word) {
-          if (lane == 0) mrow[cur_word] = cur_bits;
-          cur_word = word;
-          cur_bits = 0;
-        }
-        cur_bits |= mine << sh;
-        if (sh + (uint32_t)cvalid > 64) {
-          if (lane == 0) mrow[cur_word] = cur_bits;
-          cur_word = word + 1;
-          cur_bits = mine >> (64 - sh);
-        }
-      }
-      count += __builtin_popcountll(mine);
-      exact_blocks<D, BLK>(ktile, vtile, kh, vh, L, j0, mask0 | mask1, mine, qreg, a.c_log2,
-                           m_run, l_run, o, wave, lane);
     }
-    if (mrow && lane == 0) mrow[cur_word] = cur_bits;
-    if (a.sel_count && writer && lane == 0) a.sel_count[bh * N + i_g] = count;
+    __syncthreads();  // bitmaps complete; staging buffers free
+
+    // debug outputs: the group's first wave writes its row of the bitmap
+    if (grp_on && (wave % C::QW) == 0) {
+      const uint32_t W64 = (N + 63) / 64;
+      int count = 0;
+      for (uint32_t w = lane; w < W64; w += kWave) {
+        const uint32_t lo = selbits[grp][2 * w];
+        const uint32_t hi = (2 * w + 1 < words) ? selbits[grp][2 * w + 1] : 0u;
+        if (a.sel_mask)
+          a.sel_mask[(size_t)(bh * N + i_g) * W64 + w] = ((uint64_t)hi << 32) | lo;
+        count += __builtin_popcount(lo) + __builtin_popcount(hi);
+      }
+      if (a.sel_count) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) count += __shfl_xor(count, off);
+        if (lane == 0) a.sel_count[bh * N + i_g] = count;
+      }
+    }
+
+    // ---- inner loops: exact attention over the selected blocks, in order
+    exact_phase<D, BLK>(k0, v0, k1, v1, selbits, N, L, kh, vh, grp_on, grp, qreg, a.c_log2,
+                        m_run, l_run, o, wave, lane);
   } else {
-    for (uint32_t j0 = 0; j0 < N; j0 += 64) {
-      const uint32_t n = (N - j0) < 64 ? (N - j0) : 64;
-      const uint64_t all = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
-      exact_blocks<D, BLK>(ktile, vtile, kh, vh, L, j0, all, grp_on ? all : 0ull, qreg,
-                           a.c_log2, m_run, l_run, o, wave, lane);
-    }
+    exact_phase<D, BLK>(k0, v0, k1, v1, nullptr, N, L, kh, vh, grp_on, grp, qreg, a.c_log2,
+                        m_run, l_run, o, wave, lane);
   }
 
   // O = N / D: combine the two lane halves of the denominator.
@@ -554,6 +611,8 @@ hipError_t launch_attn(const Shape& s, AttnArgs a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t fused_max_blocks() { return kMaxBlocks; }
 
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,

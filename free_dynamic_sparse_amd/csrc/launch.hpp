@@ -25,6 +25,9 @@ hipError_t launch_pool(const Shape& s, const void* q, const void* k, const void*
 hipError_t launch_moments(const Shape& s, const float* qbar, const float* kbar, float* kmean,
                           float* kcov, float* tau, float* mu, float* sigma, hipStream_t stream);
 
+// Largest N = ceil(L / block) the fused kernel keeps on-chip selection bits for.
+int64_t fused_max_blocks();
+
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,
                       void* out, uint64_t* sel_mask, int32_t* sel_count, hipStream_t stream);

@@ -94,6 +94,7 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
   if (rc != SOLATTN_OK) return rc;
   rc = check_routing(p);
   if (rc != SOLATTN_OK) return rc;
+  if (s.N > solattn::fused_max_blocks()) return SOLATTN_E_UNSUPPORTED;
   if (empty) return SOLATTN_OK;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(qbar) || !ok_ptr(kbar) ||
       !ok_ptr(vhat) || !ok_ptr(tau) || !ok_ptr(out) || !ok_opt_ptr(sel_mask) ||
@@ -121,7 +122,8 @@ const char* solattn_strerror(int code) {
     case SOLATTN_E_INVALID_ARG:
       return "invalid argument (null or misaligned pointer, bad shape, NaN beta or scale)";
     case SOLATTN_E_UNSUPPORTED:
-      return "unsupported configuration (head_dim and block must be 64 or 128, chunk 1..64)";
+      return "unsupported configuration (head_dim and block must be 64 or 128, chunk 1..64, "
+             "and solattn_fwd needs ceil(seq_len / block) <= 8192)";
     case SOLATTN_E_HIP:
       return "HIP launch failed";
     default:

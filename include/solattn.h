@@ -128,6 +128,8 @@ int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* 
  * Nothing about the selection is written to memory unless sel_mask or
  * sel_count is given.  With SOLATTN_FLAG_EXACT_ONLY unselected blocks are
  * dropped and a row with no selected block outputs 0.
+ * Limit: N = ceil(L / block) <= 8192 (the selection bits of a query block
+ * stay on chip); larger N returns SOLATTN_E_UNSUPPORTED.
  */
 int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
                 const float* qbar, const float* kbar, const float* vhat, const float* tau,

@@ -111,6 +111,12 @@ def test_empty_problem_still_checks_beta_and_chunk(sa):
     assert call_fwd(sa, p, ptr=None) == -2
 
 
+def test_fused_block_limit(sa):
+    # the fused kernel keeps at most 8192 blocks of selection bits on chip
+    assert call_fwd(sa, sa.problem(1, 1, 8192 * 128 + 1, 128, 128, 32, 1.0)) == -2
+    assert call_fwd(sa, sa.problem(1, 1, 8192 * 64 + 1, 64, 64, 16, 1.0)) == -2
+
+
 def test_grid_limit(sa):
     # B*H*N must fit a 1-D grid (< 2^31)
     p = sa.problem(1 << 20, 1 << 10, 4096, 64, 64, 16, 1.0)
