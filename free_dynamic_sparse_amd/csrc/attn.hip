@@ -15,22 +15,25 @@
 // put two waves on every SIMD, so one wave's softmax (VALU) can overlap the
 // other's MFMA work.
 //
-// The nested loop of Algorithm 3.2, pipelined for latency:
-//   * outer loop (routing and approximation), run over all chunks first:
-//     the chunk's pooled keys Kbar_j and summed values Vhat_j are staged in
-//     LDS; every wave computes shat_ij = scale * Qbar_i . Kbar_j in float32
-//     for both groups and ballots shat_ij >= tau_i (the same instructions on
-//     the same data in every wave, so the masks agree without communication;
-//     the page reads these scores off the token-to-block tile as column
-//     means, the same number, which a bf16 tile could not resolve inside the
-//     tie band); the selected bits go to an on-chip bitmap; the unselected
-//     columns of the token-to-block tile scale * Q_i KC^T (MFMA, KC in bf16)
-//     update the group's online softmax with weight n_j and value Vhat_j.
-//   * inner loops (exact attention), then run back to back over the selected
-//     blocks of all chunks in order, so that the next block's K/V are always
-//     in flight: K and V are double-buffered in LDS, loaded with direct-to-LDS
-//     loads (global_load_lds_dwordx4, 1 KB per wave instruction) into
-//     XOR-swizzled tiles, one workgroup barrier per key block.
+// The nested loop of Algorithm 3.2, reordered for latency (the selected set
+// is the union of the chunks' sets, so the order changes nothing):
+//   * routing: every pooled key is tested against both thresholds up front
+//     (shat_ij = scale * Qbar_i . Kbar_j in float32, one key per thread; the
+//     page reads these scores off the token-to-block tile as column means,
+//     the same number, which a bf16 tile could not resolve inside the tie
+//     band); the selected bits stay in an on-chip bitmap;
+//   * approximation: the pooled keys are staged 32 at a time into LDS as
+//     bf16 tiles (Kbar in the K layout, Vhat in the V layout; the next 32 in
+//     registers meanwhile); the token-to-block tile scale * Q_i KC^T (MFMA)
+//     gives the logits of the unselected columns, which enter the group's
+//     online softmax with weight n_j and value Vhat_j;
+//   * exact attention: the selected blocks of both groups run back to back
+//     in increasing order with the next block's K/V always in flight: K and
+//     V are double-buffered in LDS, loaded with direct-to-LDS loads
+//     (global_load_lds_dwordx4, 1 KB per wave instruction) into XOR-swizzled
+//     tiles, one workgroup barrier per key block.  Each block is processed
+//     in 32-key tiles so that a tile's exponentials overlap the next tile's
+//     score MFMAs.
 // Exact and approximate terms share one running max, denominator and
 // accumulator; the order in which they enter is immaterial to the result.
 //
@@ -74,10 +77,14 @@ struct Cfg {
   static constexpr int DMA = TILE / 1024 / WAVES;  // 1 KB loads per wave per tile
   static constexpr int ROWS_1K = 1024 / ROW;       // tile rows per 1 KB load
   static constexpr int SUB = 32;            // pooled rows staged at a time
-  static constexpr int PROW = 4 * D;        // bytes per float32 pooled row
-  static constexpr int PSEGS = D / 4;       // 16-byte segments in a pooled row
+  // One LDS array: K tiles first so that every K read address fits the
+  // 16-bit instruction offset, then V tiles, then the routing state.
+  static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
+  static constexpr int BITS = 4 * TILE;                      // 2 x kMaxBlocks bits
+  static constexpr int QBAR = BITS + 2 * (kMaxBlocks / 8);  // 2 x D floats
+  static constexpr int SMEM_FUSED = QBAR + 2 * D * 4;
+  static constexpr int SMEM_DENSE = 4 * TILE;
   static_assert(DMA * WAVES * 1024 == TILE, "tile must split into whole 1 KB loads");
-  static_assert(SUB * PROW <= TILE, "a staged sub-chunk must fit one tile buffer");
 };
 
 // XOR swizzles of 16-byte segments (rows are written lane-linearly by the
@@ -89,8 +96,6 @@ template <int SEGS>
 __device__ __forceinline__ int swz_k(int r) { return r % SEGS; }
 template <int SEGS>
 __device__ __forceinline__ int swz_v(int r) { return (4 * (r % 4)) % SEGS; }
-template <int PSEGS>
-__device__ __forceinline__ int swz_p(int r) { return r % PSEGS; }
 
 struct AttnArgs {
   const uint16_t* q;
@@ -121,6 +126,12 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// s_waitcnt vmcnt(0) issued through the builtin, so that the compiler's own
+// waitcnt bookkeeping sees it: loads issued before it (the Q operand, the
+// routing inputs) count as complete inside the block loop, which then needs
+// no vector-memory wait of the compiler's own.  Encoding (gfx9): vmcnt 0,
+// expcnt 7, lgkmcnt 15.
+__device__ __forceinline__ void settle_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Workgroup barrier that does not wait for outstanding direct-to-LDS loads.
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -162,95 +173,212 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 p, float acc) {
 
 // ---------------------------------------------------------------- exact path
 
-// Issue this wave's share of the direct-to-LDS loads of one K or V tile.
-// Rows >= nkeys re-read row nkeys-1 (finite data that the softmax masks).
-template <int D, int BLK, bool IS_V>
-__device__ __forceinline__ void dma_tile(char* tile, const uint16_t* gblk, int nkeys, int wave,
-                                         int lane) {
+// Direct-to-LDS loads of K and V tiles (global_load_lds_dwordx4: each lane
+// fetches 16 bytes from global memory and the wave writes them to 1 KB of
+// LDS at M0 + 16 * lane).  The loads are issued from inline assembly so the
+// compiler does not track them: its waitcnt pass cannot tell the buffer being
+// filled from the one being read and would otherwise wait for every
+// outstanding prefetch before the first LDS read of a block.  The caller
+// waits explicitly (s_waitcnt vmcnt) before a workgroup barrier, and no other
+// vector-memory load may be outstanding while a prefetch is in flight.
+template <int D, int BLK>
+struct TileDma {
   using C = Cfg<D, BLK>;
-#pragma unroll
-  for (int c = 0; c < C::DMA; ++c) {
-    const int chunk = wave + c * C::WAVES;
-    const int row = chunk * C::ROWS_1K + lane / C::SEGS;
-    const int pos = lane % C::SEGS;
-    const int seg = pos ^ (IS_V ? swz_v<C::SEGS>(row) : swz_k<C::SEGS>(row));
-    const int grow = row < nkeys ? row : nkeys - 1;
-    const uint16_t* src = gblk + (size_t)grow * D + seg * 8;
-    __builtin_amdgcn_global_load_lds((void*)src, LDS_PTR(void, tile + chunk * 1024), 16, 0, 0);
+  uint32_t koff[C::DMA];  // byte offset in a full tile of this lane's 16 bytes (K swizzle)
+  uint32_t voff[C::DMA];  // same with the V swizzle
+
+  __device__ __forceinline__ static int row_of(int wave, int lane, int c) {
+    return (wave + c * C::WAVES) * C::ROWS_1K + lane / C::SEGS;
   }
-}
-
-template <int D, int BLK>
-__device__ __forceinline__ void dma_block(char* ktile, char* vtile, const uint16_t* kh,
-                                          const uint16_t* vh, uint32_t j, int nkeys, int wave,
-                                          int lane) {
-  dma_tile<D, BLK, false>(ktile, kh + (size_t)j * BLK * D, nkeys, wave, lane);
-  dma_tile<D, BLK, true>(vtile, vh + (size_t)j * BLK * D, nkeys, wave, lane);
-}
-
-// One key block of exact attention for this wave's 32 queries: S^T = K Q^T,
-// online-softmax update, O^T += V^T P^T.  The exponentials of P V k-step
-// kk + 1 are independent of the MFMAs of step kk, so the two overlap.
-template <int D, int BLK>
-__device__ __forceinline__ void exact_block(const char* ktile, const char* vtile,
-                                            const bf16x8* qreg, int nkeys, float c,
-                                            float& m_run, float& l_run, f32x16* o, int lane) {
-  using C = Cfg<D, BLK>;
-  const int h = lane / 32, l32 = lane % 32;
-  f32x16 s[C::MT];
+  __device__ __forceinline__ static uint32_t offset(int row, int lane, bool is_v) {
+    const int seg = (lane % C::SEGS) ^ (is_v ? swz_v<C::SEGS>(row) : swz_k<C::SEGS>(row));
+    return (uint32_t)((row * D + seg * 8) * 2);
+  }
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt) {
-      const int row = 32 * mt + l32;
-      const int seg = (2 * ks + h) ^ swz_k<C::SEGS>(row);
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ktile + row * C::ROW + seg * 16);
-      s[mt] = mfma32x32x16(ka, qreg[ks], s[mt]);
+    for (int c = 0; c < C::DMA; ++c) {
+      const int row = row_of(wave, lane, c);
+      koff[c] = offset(row, lane, false);
+      voff[c] = offset(row, lane, true);
     }
   }
-  if (nkeys < BLK) {
-    const int lim = nkeys - 4 * h;  // key 32mt + 8(r/4) + 4h + r%4 is valid iff < nkeys
-#pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (32 * mt + 8 * (r / 4) + (r % 4) >= lim) s[mt][r] = -INFINITY;
+  // The s_nop covers the M0-write to LDS-DMA hazard.
+  __device__ __forceinline__ static void load(uint32_t voffset, const uint16_t* sbase,
+                                              uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(sbase),
+                 "{m0}"(lds)
+                 : "memory");
   }
-  float mx = -INFINITY;
+  // K and V of key block j (nkeys valid rows) into the tiles at LDS byte
+  // addresses lds_k / lds_v.  Rows >= nkeys re-read row nkeys - 1 (finite
+  // data that the softmax masks).
+  __device__ __forceinline__ void block(uint32_t lds_k, uint32_t lds_v, const uint16_t* kh,
+                                        const uint16_t* vh, uint32_t j, int nkeys, int wave,
+                                        int lane) const {
+    const uint16_t* kb = kh + (size_t)j * BLK * D;
+    const uint16_t* vb = vh + (size_t)j * BLK * D;
+    if (nkeys == BLK) {
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
+      for (int c = 0; c < C::DMA; ++c)
+        load(koff[c], kb, lds_k + (uint32_t)(wave + c * C::WAVES) * 1024u);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-  mx = wave_max_pair(mx);
-  raise_max<C::DT>(mx * c, m_run, l_run, o);
-  float psum = 0.f;
-  const int g = lane / 16, j = lane % 16;
+      for (int c = 0; c < C::DMA; ++c)
+        load(voff[c], vb, lds_v + (uint32_t)(wave + c * C::WAVES) * 1024u);
+    } else {
 #pragma unroll
-  for (int kk = 0; kk < C::PK; ++kk) {
-    const int mt = kk / 2, hf = kk % 2;
-    float pv[8];
+      for (int c = 0; c < C::DMA; ++c) {
+        const int row = row_of(wave, lane, c);
+        const int back = row < nkeys ? 0 : row - (nkeys - 1);
+        load(koff[c] - (uint32_t)(back * D * 2), kb, lds_k + (uint32_t)(wave + c * C::WAVES) * 1024u);
+      }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[mt][8 * hf + e], c, -m_run));
-    const bf16x8 pk = pack_bf16x8(pv);
-    psum = sum_bf16x8(pk, psum);
-    const int row = 16 * kk + 4 * (g / 2) + j / 4;
+      for (int c = 0; c < C::DMA; ++c) {
+        const int row = row_of(wave, lane, c);
+        const int back = row < nkeys ? 0 : row - (nkeys - 1);
+        load(voff[c] - (uint32_t)(back * D * 2), vb, lds_v + (uint32_t)(wave + c * C::WAVES) * 1024u);
+      }
+    }
+  }
+};
+
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+
+// Per-lane byte offsets, within a tile, of this lane's MFMA operand reads.
+// They do not depend on the 32-key tile mt or the P V k-step kk (the
+// swizzles repeat with period 16 rows for K and 4 rows for V), which enter
+// as compile-time offsets.
+template <int D, int BLK>
+struct LaneOffsets {
+  using C = Cfg<D, BLK>;
+  uint32_t k[C::KS];  // K row 32 mt + lane % 32, d = 16 ks + 8 (lane / 32) .. + 7
+  uint32_t v[C::DT];  // transpose-read address for d tile dt (rows 16 kk + ...) in V buffer 0
+  __device__ __forceinline__ void init(int lane) {
+    const int h = lane / 32, l32 = lane % 32;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      k[ks] = (uint32_t)(l32 * C::ROW + ((2 * ks + h) ^ swz_k<C::SEGS>(l32)) * 16);
+    const int g = lane / 16, j = lane % 16;
+    const int r0 = 4 * (g / 2) + j / 4;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       const int col = 32 * dt + 16 * (g % 2) + 4 * (j % 4);
-      const char* p0 =
-          vtile + row * C::ROW + ((col / 8) ^ swz_v<C::SEGS>(row)) * 16 + (col % 8) * 2;
-      // keys 16kk + 4h + {0..3} and 16kk + 8 + 4h + {0..3} for d = 32dt + lane%32
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0 + 8 * C::ROW));
-      const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pk, o[dt]);
+      v[dt] = (uint32_t)(C::V0 + r0 * C::ROW + ((col / 8) ^ swz_v<C::SEGS>(r0)) * 16 +
+                         (col % 8) * 2);
     }
   }
-  l_run += psum;
+};
+
+// S^T tile mt (keys 32 mt .. 32 mt + 31 of the block) = K Q^T for this
+// wave's 32 queries: lane l holds query l % 32 against keys
+// 32 mt + mfma_row(r, l / 32).
+template <int D, int BLK>
+__device__ __forceinline__ f32x16 score_tile(const char* ktile, const LaneOffsets<D, BLK>& off,
+                                             const bf16x8* qreg, int mt) {
+  using C = Cfg<D, BLK>;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const bf16x8 ka =
+        *reinterpret_cast<const bf16x8*>(ktile + 32 * mt * C::ROW + off.k[ks]);
+    acc = mfma32x32x16(ka, qreg[ks], acc);
+  }
+  return acc;
+}
+
+// O^T += V^T P^T for P V k-step kk (keys 16 kk + {4h..4h+3, 8+4h..8+4h+3},
+// the keys whose probabilities pk holds).  vtile points V1 - V0 bytes past
+// the start of V buffer 0 for buffer 1 (the lane offsets include V0), so
+// every address below is a lane offset plus a compile-time constant.
+template <int D, int BLK>
+__device__ __forceinline__ void pv_step(const char* vtile, const LaneOffsets<D, BLK>& off,
+                                        bf16x8 pk, int kk, f32x16* o) {
+  using C = Cfg<D, BLK>;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const char* p0 = vtile + 16 * kk * C::ROW + off.v[dt];
+    // keys 16kk + 4h + {0..3} and 16kk + 8 + 4h + {0..3} for d = 32dt + lane%32
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0 + 8 * C::ROW));
+    const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pk, o[dt]);
+  }
+}
+
+// Probabilities of one S^T tile against the running max: p = 2^(c s - m),
+// packed to bf16 for the P V product; returns the row-partial sum of the
+// packed values (what the numerator sees).
+__device__ __forceinline__ float tile_probs(const f32x16& s, float c, float m, bf16x8* pk0,
+                                            bf16x8* pk1) {
+  float p[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) p[e] = fast_exp2(__builtin_fmaf(s[e], c, -m));
+  *pk0 = pack_bf16x8(p);
+  *pk1 = pack_bf16x8(p + 8);
+  return sum_bf16x8(*pk1, sum_bf16x8(*pk0, 0.f));
+}
+
+// A tile's probabilities may exceed 1 by up to this factor before the
+// running max is raised (they stay far from float32 overflow; bf16 and
+// float32 keep their relative precision at any magnitude).
+constexpr float kMaxTileSum = 0x1p40f;
+
+// One key block of exact attention for this wave's 32 queries, streamed in
+// 32-key tiles: the scores of tile mt + 1 (MFMA) are computed while tile
+// mt's probabilities (VALU) are formed, and tile mt then enters O^T.  The
+// running max is not recomputed per tile: the probabilities are formed
+// against the current max and only when a tile's sum leaves [0, 2^40] (or
+// is not finite, as on the very first tile) is the max raised to the tile's
+// maximum, the state rescaled and the tile redone.  Normalising by the same
+// denominator keeps the result exact whatever reference max is used.
+// TAIL: the block has nkeys < BLK valid keys (the last block of a head);
+// a separate instantiation keeps the masking out of the common path's basic
+// blocks so the scheduler can interleave tile mt + 1's MFMAs with tile mt's
+// exponentials.
+template <int D, int BLK, bool TAIL>
+__device__ __forceinline__ void exact_block(const char* ktile, const char* vtile,
+                                            const LaneOffsets<D, BLK>& off, const bf16x8* qreg,
+                                            int nkeys, float c, float& m_run, float& l_run,
+                                            f32x16* o, int lane) {
+  using C = Cfg<D, BLK>;
+  const int h = lane / 32;
+  f32x16 s = score_tile<D, BLK>(ktile, off, qreg, 0);
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt) {
+    f32x16 s_next;
+    if (mt + 1 < C::MT) s_next = score_tile<D, BLK>(ktile, off, qreg, mt + 1);
+    if (TAIL) {
+      const int lim = nkeys - 32 * mt - 4 * h;  // key 32mt + 8(r/4) + 4h + r%4 valid iff < nkeys
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r / 4) + (r % 4) >= lim) s[r] = -INFINITY;
+    }
+    bf16x8 pk0, pk1;
+    float ps = tile_probs(s, c, m_run, &pk0, &pk1);
+    if (__builtin_expect(__ballot(!(ps <= kMaxTileSum)) != 0, 0)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = wave_max_pair(mx) * c;
+      float m_new = fmaxf(m_run, mx);
+      if (m_new == -INFINITY) m_new = 0.f;  // nothing valid yet: any finite reference
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+      ps = tile_probs(s, c, m_run, &pk0, &pk1);
+    }
+    l_run += ps;
+    pv_step<D, BLK>(vtile, off, pk0, 2 * mt, o);
+    pv_step<D, BLK>(vtile, off, pk1, 2 * mt + 1, o);
+    if (mt + 1 < C::MT) s = s_next;
+  }
 }
 
 // Iterates, in increasing order, over the blocks whose bit is set in the
@@ -274,15 +402,19 @@ struct BlockWalker {
 };
 
 // Exact attention over every block of the union bitmap (or all N blocks
-// when `bits` is null: the dense kernel), double-buffered.  Group grp takes
-// the blocks whose bit is set in its own bitmap.
+// when `bits` is null: the dense kernel), double-buffered in LDS: block j is
+// computed from one buffer while block j+1 streams into the other, one
+// workgroup barrier per block.  Group grp takes the blocks whose bit is set
+// in its own bitmap.  Only the last block of a head can be partial; it is
+// always the last one visited and is computed after the loop, so the loop
+// body carries no masking.
 template <int D, int BLK>
-__device__ __forceinline__ void exact_phase(char* k0, char* v0, char* k1, char* v1,
-                                            const uint32_t (*bits)[kMaxBlocks / 32],
+__device__ __forceinline__ void exact_phase(char* smem, const uint32_t (*bits)[kMaxBlocks / 32],
                                             uint32_t N, int64_t L, const uint16_t* kh,
                                             const uint16_t* vh, bool grp_on, int grp,
                                             const bf16x8* qreg, float c, float& m_run,
                                             float& l_run, f32x16* o, int wave, int lane) {
+  using C = Cfg<D, BLK>;
   auto nkeys_of = [&](uint32_t j) {
     const int64_t rem = L - (int64_t)j * BLK;
     return (int)(rem < BLK ? rem : BLK);
@@ -302,116 +434,157 @@ __device__ __forceinline__ void exact_phase(char* k0, char* v0, char* k1, char* 
     *j = dense_next++;
     return true;
   };
+  settle_vm();
+  LaneOffsets<D, BLK> off;
+  off.init(lane);
+  TileDma<D, BLK> dma;
+  dma.init(wave, lane);
+  const uint32_t base = lds_addr(smem);
+  const uint32_t lk0 = base + C::K0, lv0 = base + C::V0;
+  const uint32_t lk1 = base + C::K1, lv1 = base + C::V1;
   uint32_t j;
   if (!next(&j)) return;
-  dma_block<D, BLK>(k0, v0, kh, vh, j, nkeys_of(j), wave, lane);
+  dma.block(lk0, lv0, kh, vh, j, nkeys_of(j), wave, lane);
+  bool tail = false;
+  int tail_buf = 0;
   while (true) {
     // even step: compute from buffer 0, prefetch into buffer 1
     uint32_t jn;
     bool more = next(&jn);
     wait_vm<0>();
     barrier_lds();  // block j is in buffer 0; everyone is done with buffer 1
-    if (more) dma_block<D, BLK>(k1, v1, kh, vh, jn, nkeys_of(jn), wave, lane);
-    if (active_for(j)) exact_block<D, BLK>(k0, v0, qreg, nkeys_of(j), c, m_run, l_run, o, lane);
+    if (more) dma.block(lk1, lv1, kh, vh, jn, nkeys_of(jn), wave, lane);
+    if (nkeys_of(j) < BLK) { tail = true; tail_buf = 0; break; }
+    if (active_for(j))
+      exact_block<D, BLK, false>(smem + C::K0, smem, off, qreg, BLK, c, m_run, l_run, o, lane);
     if (!more) break;
     j = jn;
     // odd step: compute from buffer 1, prefetch into buffer 0
     more = next(&jn);
     wait_vm<0>();
     barrier_lds();
-    if (more) dma_block<D, BLK>(k0, v0, kh, vh, jn, nkeys_of(jn), wave, lane);
-    if (active_for(j)) exact_block<D, BLK>(k1, v1, qreg, nkeys_of(j), c, m_run, l_run, o, lane);
+    if (more) dma.block(lk0, lv0, kh, vh, jn, nkeys_of(jn), wave, lane);
+    if (nkeys_of(j) < BLK) { tail = true; tail_buf = 1; break; }
+    if (active_for(j))
+      exact_block<D, BLK, false>(smem + C::K1, smem + (C::V1 - C::V0), off, qreg, BLK, c, m_run,
+                                 l_run, o, lane);
     if (!more) break;
     j = jn;
+  }
+  if (tail && active_for(j)) {
+    const int kb = tail_buf ? C::K1 : C::K0, vb = tail_buf ? C::V1 - C::V0 : 0;
+    exact_block<D, BLK, true>(smem + kb, smem + vb, off, qreg, nkeys_of(j), c, m_run, l_run, o,
+                              lane);
   }
   barrier_lds();  // buffers free for whoever comes next
 }
 
 // ---------------------------------------------------------- routing / approx
 
-// Stage pooled rows [j0, j0 + rows) of Kbar into kst and Vhat into vst
-// (float32, swizzled 16-byte segments); the rest of the SUB rows are zero so
-// readers need no bounds checks.
+// Routing of every pooled key for both query blocks of the pair: bit j of
+// bits[g] is set iff shat_gj = scale * Qbar_g . Kbar_j >= tau_g (Eq. 4).
+// The page streams this test chunk by chunk inside the outer loop; since the
+// selected set is the union of the chunks' sets (the chunk-wise streaming
+// identity), the kernel runs the whole row up front, one pooled key per
+// thread with a float32 dot product in order of d, and the exact blocks then
+// stream back to back.  Each wave covers 64 consecutive keys, so the words it
+// writes are its own.
 template <int D, int BLK>
-__device__ __forceinline__ void stage_pooled(char* kst, char* vst, const float* kbar_h,
-                                             const float* vhat_h, uint32_t j0, int rows,
-                                             int tid) {
+__device__ __forceinline__ void route_all(uint32_t (*bits)[kMaxBlocks / 32],
+                                          const float (*qbar_s)[D], const float* kbar_h,
+                                          uint32_t N, float tau0, float tau1, float scale,
+                                          int tid, int lane) {
   using C = Cfg<D, BLK>;
-  constexpr int IT = (C::SUB * C::PSEGS + C::NT - 1) / C::NT;
+  for (uint32_t j0 = tid - lane; j0 < N; j0 += C::NT) {
+    const uint32_t j = j0 + lane;
+    float d0 = 0.f, d1 = 0.f;
+    if (j < N) {
+      const float* kr = kbar_h + (size_t)j * D;
+#pragma unroll 8
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + e);
+        const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][e]);
+        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][e]);
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = tid + it * C::NT;
-    const int jj = idx / C::PSEGS, sg = idx % C::PSEGS;
-    if (jj < C::SUB) {
-      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (jj < rows) {
-        const size_t gofs = (size_t)(j0 + jj) * D + sg * 4;
-        kk = *reinterpret_cast<const f32x4*>(kbar_h + gofs);
-        vv = *reinterpret_cast<const f32x4*>(vhat_h + gofs);
+        for (int x = 0; x < 4; ++x) {
+          d0 = __builtin_fmaf(q0[x], kv[x], d0);
+          d1 = __builtin_fmaf(q1[x], kv[x], d1);
+        }
       }
-      const int at = jj * C::PROW + (sg ^ swz_p<C::PSEGS>(jj)) * 16;
-      *reinterpret_cast<f32x4*>(kst + at) = kk;
-      *reinterpret_cast<f32x4*>(vst + at) = vv;
+    }
+    const uint64_t b0 = __ballot(j < N && scale * d0 >= tau0);
+    const uint64_t b1 = __ballot(j < N && scale * d1 >= tau1);
+    if (lane == 0) {
+      bits[0][j0 / 32] = (uint32_t)b0;
+      bits[0][j0 / 32 + 1] = (uint32_t)(b0 >> 32);
+      bits[1][j0 / 32] = (uint32_t)b1;
+      bits[1][j0 / 32 + 1] = (uint32_t)(b1 >> 32);
     }
   }
 }
 
+// One thread's share of a sub-chunk of SUB = 32 pooled rows (Kbar and Vhat,
+// float32 in global memory), held in registers between its load and its
+// bf16 store into LDS: the K rows in the K-tile layout (so score_tile reads
+// them as a 32-key tile) and the V rows in the V-tile layout (so pv_step
+// reads them as two 16-key k-steps).  Rows past the head's last block are 0.
 template <int D, int BLK>
-__device__ __forceinline__ const float* pooled_at(const char* st, int row, int col) {
+struct PooledStage {
   using C = Cfg<D, BLK>;
-  return reinterpret_cast<const float*>(st + row * C::PROW +
-                                        ((col / 4) ^ swz_p<C::PSEGS>(row)) * 16) +
-         (col % 4);
-}
-
-// Routing of up to 32 staged pooled keys for both query blocks of the pair:
-// bit jj of mask g is set iff pooled key jj (< rows) has shat >= tau_g.
-template <int D, int BLK>
-__device__ __forceinline__ void route_sub(const char* kst, const float (*qbar_s)[D], int rows,
-                                          float tau0, float tau1, float scale, int lane,
-                                          uint32_t* m0, uint32_t* m1) {
-  constexpr int HALF = D / 2;
-  const int h = lane / 32, jj = lane % 32;
-  float p0 = 0.f, p1 = 0.f;
+  static constexpr int Q4 = D / 4;                       // float4 per row
+  static constexpr int PER = C::SUB * Q4 / C::NT;        // float4 per thread per array
+  static_assert(PER * C::NT == C::SUB * Q4, "sub-chunk must split evenly");
+  f32x4 k[PER], v[PER];
+  __device__ __forceinline__ void load(const float* kbar_h, const float* vhat_h, uint32_t jb,
+                                       uint32_t N, int tid) {
 #pragma unroll
-  for (int e = 0; e < HALF; e += 4) {
-    const f32x4 kv = *reinterpret_cast<const f32x4*>(pooled_at<D, BLK>(kst, jj, h * HALF + e));
-    const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][h * HALF + e]);
-    const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][h * HALF + e]);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      p0 = __builtin_fmaf(q0[x], kv[x], p0);
-      p1 = __builtin_fmaf(q1[x], kv[x], p1);
+    for (int c = 0; c < PER; ++c) {
+      const int idx = tid + c * C::NT, row = idx / Q4, q4 = idx % Q4;
+      f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+      if (jb + row < N) {
+        const size_t g = (size_t)(jb + row) * D + 4 * q4;
+        kk = *reinterpret_cast<const f32x4*>(kbar_h + g);
+        vv = *reinterpret_cast<const f32x4*>(vhat_h + g);
+      }
+      k[c] = kk;
+      v[c] = vv;
     }
   }
-  const float o0 = __shfl_xor(p0, 32), o1 = __shfl_xor(p1, 32);
-  const float d0 = (h == 0) ? (p0 + o0) : (o0 + p0);
-  const float d1 = (h == 0) ? (p1 + o1) : (o1 + p1);
-  *m0 = (uint32_t)__ballot((jj < rows) && (scale * d0 >= tau0));
-  *m1 = (uint32_t)__ballot((jj < rows) && (scale * d1 >= tau1));
-}
-
-// Zeroth-order terms of the staged pooled keys whose bit is set in unsel
-// (Eqs. 9-10): logits from the token-to-block tile, weight n_j in the
-// denominator, Vhat_j in the numerator.  jbase = index of staged row 0.
-template <int D, int BLK>
-__device__ __forceinline__ void approx_sub(const char* kst, const char* vst, const bf16x8* qreg,
-                                           uint32_t unsel, uint32_t jbase, uint32_t N,
-                                           int n_last, float c, float& m_run, float& l_run,
-                                           f32x16* o, int lane) {
-  using C = Cfg<D, BLK>;
-  const int h = lane / 32, l32 = lane % 32;
-  f32x16 t;
+  __device__ __forceinline__ void store(char* kt, char* vt, int tid) const {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) t[r] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    // staged row l32 (finite; zero past the staged rows) feeds this lane's A operand
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(pooled_at<D, BLK>(kst, l32, 16 * ks + 8 * h));
-    const f32x4 a1 =
-        *reinterpret_cast<const f32x4*>(pooled_at<D, BLK>(kst, l32, 16 * ks + 8 * h + 4));
-    t = mfma32x32x16(pack_bf16x8(a0, a1), qreg[ks], t);
+    for (int c = 0; c < PER; ++c) {
+      const int idx = tid + c * C::NT, row = idx / Q4, d = 4 * (idx % Q4);
+      const int byte = (d % 8) * 2;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      auto pack4 = [](f32x4 x) {
+        u32x2 r;
+        r[0] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[0]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[1]) << 16);
+        r[1] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[2]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[3]) << 16);
+        return r;
+      };
+      *reinterpret_cast<u32x2*>(kt + row * C::ROW + ((d / 8) ^ swz_k<C::SEGS>(row)) * 16 + byte) =
+          pack4(k[c]);
+      *reinterpret_cast<u32x2*>(vt + row * C::ROW + ((d / 8) ^ swz_v<C::SEGS>(row)) * 16 + byte) =
+          pack4(v[c]);
+    }
   }
+};
+
+// Zeroth-order terms (Eqs. 9-10) of the staged pooled keys whose bit is set
+// in unsel, for this wave's 32 queries: logits scale * q_r . Kbar_j from the
+// token-to-block tile (Eq. 11; MFMA on bf16 Kbar), denominator weight n_j,
+// numerator Vhat_j.  jb = pooled key of staged row 0.
+template <int D, int BLK>
+__device__ __forceinline__ void approx_sub(const char* kt, const char* vt,
+                                           const LaneOffsets<D, BLK>& off, const bf16x8* qreg,
+                                           uint32_t unsel, uint32_t jb, uint32_t N, int n_last,
+                                           float c, float& m_run, float& l_run, f32x16* o,
+                                           int lane) {
+  using C = Cfg<D, BLK>;
+  const int h = lane / 32;
+  f32x16 t = score_tile<D, BLK>(kt, off, qreg, 0);
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -420,29 +593,65 @@ __device__ __forceinline__ void approx_sub(const char* kst, const char* vst, con
   }
   mx = wave_max_pair(mx);
   raise_max<C::DT>(mx * c, m_run, l_run, o);
+  bf16x8 pk0, pk1;
+  tile_probs(t, c, m_run, &pk0, &pk1);
   float lsum = 0.f;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(t[8 * hf + e], c, -m_run));
-    const bf16x8 pk = pack_bf16x8(pv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // weight n_j of the block behind pooled key jbase + row (bf16 P, as the numerator)
-      const float w = (jbase + mfma_row(8 * hf + e, h) == N - 1) ? (float)n_last : (float)BLK;
-      lsum = __builtin_fmaf(w, (float)pk[e], lsum);
-    }
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      float vv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)  // columns outside unsel carry p = 0 against finite values
-        vv[e] = *pooled_at<D, BLK>(vst, mfma_row(8 * hf + e, h), 32 * dt + l32);
-      o[dt] = mfma32x32x16(pack_bf16x8(vv), pk, o[dt]);
-    }
+  for (int r = 0; r < 16; ++r) {
+    // weight n_j of the block behind pooled key jb + row (bf16 P, as the numerator)
+    const float w = (jb + mfma_row(r, h) == N - 1) ? (float)n_last : (float)BLK;
+    lsum = __builtin_fmaf(w, (float)(r < 8 ? pk0[r] : pk1[r - 8]), lsum);
   }
+  pv_step<D, BLK>(vt, off, pk0, 0, o);
+  pv_step<D, BLK>(vt, off, pk1, 1, o);
   l_run += lsum;
+}
+
+// The approximation pass over all sub-chunks of 32 pooled keys that hold an
+// unselected block of either query block, with the next sub-chunk's rows
+// loaded into registers while the current one is used (one barrier each).
+// Staging buffers: halves of the second K and V tiles.
+template <int D, int BLK>
+__device__ __forceinline__ void approx_phase(char* smem, const uint32_t (*bits)[kMaxBlocks / 32],
+                                             bool pair1_on, const float* kbar_h,
+                                             const float* vhat_h, uint32_t N, int n_last,
+                                             bool grp_on, int grp, const bf16x8* qreg, float c,
+                                             float& m_run, float& l_run, f32x16* o, int tid,
+                                             int lane) {
+  using C = Cfg<D, BLK>;
+  constexpr int STAGE = C::SUB * C::ROW;  // bytes of one staged bf16 sub-chunk
+  static_assert(2 * STAGE <= C::TILE, "two staged sub-chunks must fit one tile buffer");
+  const uint32_t nsub = (N + C::SUB - 1) / C::SUB;
+  auto unsel_of = [&](int g, uint32_t sb) {
+    const uint32_t rows = N - sb * C::SUB;
+    const uint32_t valid = rows >= 32 ? 0xffffffffu : ((1u << rows) - 1u);
+    return (g == 1 && !pair1_on) ? 0u : (valid & ~bits[g][sb]);
+  };
+  auto next_needed = [&](uint32_t sb) {
+    while (sb < nsub && (unsel_of(0, sb) | unsel_of(1, sb)) == 0u) ++sb;
+    return sb;
+  };
+  LaneOffsets<D, BLK> off;
+  off.init(lane);
+  PooledStage<D, BLK> st;
+  uint32_t sb = next_needed(0);
+  if (sb < nsub) st.load(kbar_h, vhat_h, sb * C::SUB, N, tid);
+  int buf = 0;
+  while (sb < nsub) {
+    const uint32_t nb = next_needed(sb + 1);
+    char* kt = smem + C::K1 + buf * STAGE;
+    char* vt = smem + C::V1 + buf * STAGE;
+    st.store(kt, vt, tid);
+    if (nb < nsub) st.load(kbar_h, vhat_h, nb * C::SUB, N, tid);
+    __syncthreads();  // staged rows visible; the other buffer's readers are done
+    const uint32_t unsel = unsel_of(grp, sb);
+    if (grp_on && unsel)
+      approx_sub<D, BLK>(kt, vt - C::V0, off, qreg, unsel, sb * C::SUB, N, n_last, c, m_run,
+                         l_run, o, lane);
+    buf ^= 1;
+    sb = nb;
+  }
+  __syncthreads();  // staging buffers free
 }
 
 // ------------------------------------------------------------------ kernel
@@ -450,12 +659,11 @@ __device__ __forceinline__ void approx_sub(const char* kst, const char* vst, con
 template <int D, int BLK, bool FUSED>
 __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) char k0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char v0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char k1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char v1[C::TILE];
-  __shared__ uint32_t selbits[FUSED ? 2 : 1][FUSED ? kMaxBlocks / 32 : 1];
-  __shared__ __attribute__((aligned(16))) float qbar_s[FUSED ? 2 : 1][D];
+  __shared__ __attribute__((aligned(1024))) char smem[FUSED ? C::SMEM_FUSED : C::SMEM_DENSE];
+  char* const k1 = smem + C::K1;  // the routing / approximation phase stages pooled rows
+  char* const v1 = smem + C::V1;  // in the second K / V buffers
+  auto selbits = reinterpret_cast<uint32_t(*)[kMaxBlocks / 32]>(smem + C::BITS);
+  auto qbar_s = reinterpret_cast<float(*)[D]>(smem + C::QBAR);
 
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int grp = wave / C::QW;  // which block of the pair
@@ -493,7 +701,7 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
   if constexpr (FUSED) {
-    // ---- outer loop: routing and approximation over every chunk
+    // ---- outer loop: routing of every pooled key, then the approximation
     const uint32_t item0 = bh * N + 2 * pair;
     const float tau0 = a.tau[item0];
     const float tau1 = pair1_on ? a.tau[item0 + 1] : INFINITY;
@@ -503,40 +711,15 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
           (gq == 0 || pair1_on) ? a.qbar[(size_t)(item0 + gq) * D + cc % D] : 0.f;
     }
     const uint32_t words = (N + 31) / 32;
-    for (uint32_t w = tid; w < 2 * words; w += C::NT) selbits[w / words][w % words] = 0u;
     const float* kbar_h = a.kbar + (size_t)bh * N * D;
     const float* vhat_h = a.vhat + (size_t)bh * N * D;
-    const int n_last = (int)(L - (int64_t)(N - 1) * BLK);
-    const uint32_t chunk = (uint32_t)a.chunk;
-    for (uint32_t j0 = 0; j0 < N; j0 += chunk) {
-      const int cvalid = (int)((N - j0) < chunk ? (N - j0) : chunk);
-      for (int sb = 0; sb < cvalid; sb += C::SUB) {
-        const int rows = (cvalid - sb) < C::SUB ? (cvalid - sb) : C::SUB;
-        const uint32_t jb = j0 + sb;  // pooled key of staged row 0
-        __syncthreads();  // previous readers of the staging buffers are done
-        stage_pooled<D, BLK>(k1, v1, kbar_h, vhat_h, jb, rows, tid);
-        __syncthreads();
-        uint32_t s0, s1;
-        route_sub<D, BLK>(k1, qbar_s, rows, tau0, tau1, a.scale, lane, &s0, &s1);
-        if (!pair1_on) s1 = 0u;
-        if (tid == 0) {  // append to the bitmaps (single writer, in order)
-          const uint32_t wd = jb / 32, sh = jb % 32;
-          selbits[0][wd] |= s0 << sh;
-          selbits[1][wd] |= s1 << sh;
-          if (sh != 0 && sh + (uint32_t)rows > 32) {
-            selbits[0][wd + 1] |= s0 >> (32 - sh);
-            selbits[1][wd + 1] |= s1 >> (32 - sh);
-          }
-        }
-        const uint32_t mine = grp == 0 ? s0 : s1;
-        const uint32_t valid = rows >= 32 ? 0xffffffffu : ((1u << rows) - 1u);
-        const uint32_t unsel = valid & ~mine;
-        if (grp_on && !a.exact_only && unsel)
-          approx_sub<D, BLK>(k1, v1, qreg, unsel, jb, N, n_last, a.c_log2, m_run, l_run, o,
-                             lane);
-      }
-    }
-    __syncthreads();  // bitmaps complete; staging buffers free
+    __syncthreads();
+    route_all<D, BLK>(selbits, qbar_s, kbar_h, N, tau0, tau1, a.scale, tid, lane);
+    __syncthreads();  // bitmaps complete
+    if (!a.exact_only)
+      approx_phase<D, BLK>(smem, selbits, pair1_on, kbar_h, vhat_h, N,
+                           (int)(L - (int64_t)(N - 1) * BLK), grp_on, grp, qreg, a.c_log2, m_run,
+                           l_run, o, tid, lane);
 
     // debug outputs: the group's first wave writes its row of the bitmap
     if (grp_on && (wave % C::QW) == 0) {
@@ -557,10 +740,10 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
     }
 
     // ---- inner loops: exact attention over the selected blocks, in order
-    exact_phase<D, BLK>(k0, v0, k1, v1, selbits, N, L, kh, vh, grp_on, grp, qreg, a.c_log2,
+    exact_phase<D, BLK>(smem, selbits, N, L, kh, vh, grp_on, grp, qreg, a.c_log2,
                         m_run, l_run, o, wave, lane);
   } else {
-    exact_phase<D, BLK>(k0, v0, k1, v1, nullptr, N, L, kh, vh, grp_on, grp, qreg, a.c_log2,
+    exact_phase<D, BLK>(smem, nullptr, N, L, kh, vh, grp_on, grp, qreg, a.c_log2,
                         m_run, l_run, o, wave, lane);
   }
 
