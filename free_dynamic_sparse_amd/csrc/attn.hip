@@ -291,23 +291,39 @@ __device__ __forceinline__ f32x16 score_tile(const char* ktile, const LaneOffset
   return acc;
 }
 
-// O^T += V^T P^T for P V k-step kk (keys 16 kk + {4h..4h+3, 8+4h..8+4h+3},
-// the keys whose probabilities pk holds).  vtile points V1 - V0 bytes past
-// the start of V buffer 0 for buffer 1 (the lane offsets include V0), so
-// every address below is a lane offset plus a compile-time constant.
+// V^T operand fragments of P V k-step kk (keys 16 kk + {4h..4h+3,
+// 8+4h..8+4h+3}, the keys whose probabilities a tile's pk holds), one per
+// 32-wide d tile.  vtile points V1 - V0 bytes past the start of V buffer 0
+// for buffer 1 (the lane offsets include V0), so every address below is a
+// lane offset plus a compile-time constant.
+template <int D, int BLK>
+struct VFrag {
+  using C = Cfg<D, BLK>;
+  bf16x8 a[C::DT];
+  __device__ __forceinline__ void fetch(const char* vtile, const LaneOffsets<D, BLK>& off,
+                                        int kk) {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const char* p0 = vtile + 16 * kk * C::ROW + off.v[dt];
+      // keys 16kk + 4h + {0..3} and 16kk + 8 + 4h + {0..3} for d = 32dt + lane%32
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0 + 8 * C::ROW));
+      a[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+  // O^T += V^T P^T for this k-step
+  __device__ __forceinline__ void apply(bf16x8 pk, f32x16* o) const {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) o[dt] = mfma32x32x16(a[dt], pk, o[dt]);
+  }
+};
+
 template <int D, int BLK>
 __device__ __forceinline__ void pv_step(const char* vtile, const LaneOffsets<D, BLK>& off,
                                         bf16x8 pk, int kk, f32x16* o) {
-  using C = Cfg<D, BLK>;
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
-    const char* p0 = vtile + 16 * kk * C::ROW + off.v[dt];
-    // keys 16kk + 4h + {0..3} and 16kk + 8 + 4h + {0..3} for d = 32dt + lane%32
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, p0 + 8 * C::ROW));
-    const v8i16 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pk, o[dt]);
-  }
+  VFrag<D, BLK> f;
+  f.fetch(vtile, off, kk);
+  f.apply(pk, o);
 }
 
 // Probabilities of one S^T tile against the running max: p = 2^(c s - m),
@@ -352,6 +368,11 @@ __device__ __forceinline__ void exact_block(const char* ktile, const char* vtile
   for (int mt = 0; mt < C::MT; ++mt) {
     f32x16 s_next;
     if (mt + 1 < C::MT) s_next = score_tile<D, BLK>(ktile, off, qreg, mt + 1);
+    // this tile's V operands, fetched ahead so the softmax below covers the
+    // LDS latency
+    VFrag<D, BLK> va, vb;
+    va.fetch(vtile, off, 2 * mt);
+    vb.fetch(vtile, off, 2 * mt + 1);
     if (TAIL) {
       const int lim = nkeys - 32 * mt - 4 * h;  // key 32mt + 8(r/4) + 4h + r%4 valid iff < nkeys
 #pragma unroll
@@ -375,8 +396,8 @@ __device__ __forceinline__ void exact_block(const char* ktile, const char* vtile
       ps = tile_probs(s, c, m_run, &pk0, &pk1);
     }
     l_run += ps;
-    pv_step<D, BLK>(vtile, off, pk0, 2 * mt, o);
-    pv_step<D, BLK>(vtile, off, pk1, 2 * mt + 1, o);
+    va.apply(pk0, o);
+    vb.apply(pk1, o);
     if (mt + 1 < C::MT) s = s_next;
   }
 }
