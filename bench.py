@@ -84,24 +84,31 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w: synth.Workload, beta: float):
-    """The CPU oracle on one head of the workload (all its query blocks)."""
+def cpu_baseline(w: synth.Workload, beta: float, heads: int = 3):
+    """The CPU oracle on the first `heads` heads of the workload (pooling,
+    moments, thresholds, selection and every query block's output): a
+    bounded sample of about 10-20 s of host work, scaled to executed TFLOP/s."""
     from threadpoolctl import threadpool_info
 
     from oracle import solattn_ref as ref
 
-    q, k, v = synth.make_head(w, 0, 0)
-    t0 = time.perf_counter()
-    r = ref.solattn_head(q, k, v, beta, w.block, rows=[])
-    for i in range(w.N):
-        ref.forward_block(q, k, v, r.kbar, r.vhat, r.sel[i], i, w.block, r.scale)
-    dt = time.perf_counter() - t0
-    ex, tile, ap = executed_flops(r.sel[None], w.L, w.d, w.block)
+    heads = min(heads, w.H)
+    flops, dt = 0.0, 0.0
+    for h in range(heads):
+        q, k, v = synth.make_head(w, 0, h)
+        t0 = time.perf_counter()
+        r = ref.solattn_head(q, k, v, beta, w.block, rows=[])
+        for i in range(w.N):
+            ref.forward_block(q, k, v, r.kbar, r.vhat, r.sel[i], i, w.block, r.scale)
+        dt += time.perf_counter() - t0
+        ex, tile, ap = executed_flops(r.sel[None], w.L, w.d, w.block)
+        flops += ex + tile + ap
     threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    return {"value": (ex + tile + ap) / dt / 1e12, "unit": "TFLOP/s (executed)",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s (executed)",
             "cores": int(threads), "kind": "oracle",
-            "sample": f"head 0 of {w.H}: pooling, moments, thresholds, selection and all "
-                      f"{w.N} query blocks' outputs, float64 NumPy; {dt:.1f} s",
+            "sample": f"heads 0-{heads - 1} of {w.H} at beta={beta}: pooling, moments, "
+                      f"thresholds, selection and all {w.N} query blocks' outputs per head, "
+                      f"float64 NumPy; {dt:.1f} s",
             "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
 
 
