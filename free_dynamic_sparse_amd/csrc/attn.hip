@@ -686,7 +686,8 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   auto selbits = reinterpret_cast<uint32_t(*)[kMaxBlocks / 32]>(smem + C::BITS);
   auto qbar_s = reinterpret_cast<float(*)[D]>(smem + C::QBAR);
 
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int grp = wave / C::QW;  // which block of the pair
   const int h = lane / 32, l32 = lane % 32;
   uint32_t bh, pair;
