@@ -76,13 +76,14 @@ struct Cfg {
   static constexpr int TILE = BLK * ROW;    // bytes per K or V tile
   static constexpr int DMA = TILE / 1024 / WAVES;  // 1 KB loads per wave per tile
   static constexpr int ROWS_1K = 1024 / ROW;       // tile rows per 1 KB load
-  static constexpr int SUB = 32;            // pooled rows staged at a time
+  static constexpr int SUB = 64;            // pooled rows staged at a time
   // One LDS array: K tiles first so that every K read address fits the
   // 16-bit instruction offset, then V tiles, then the routing state.
   static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
   static constexpr int BITS = 4 * TILE;                      // 2 x kMaxBlocks bits
   static constexpr int QBAR = BITS + 2 * (kMaxBlocks / 8);  // 2 x D floats
-  static constexpr int SMEM_FUSED = QBAR + 2 * D * 4;
+  static constexpr int DOTS = QBAR + 2 * D * 4;              // 2 x 2 x SUB floats
+  static constexpr int SMEM_FUSED = DOTS + 2 * 2 * SUB * 4;
   static constexpr int SMEM_DENSE = 4 * TILE;
   static_assert(DMA * WAVES * 1024 == TILE, "tile must split into whole 1 KB loads");
 };
@@ -502,65 +503,54 @@ __device__ __forceinline__ void exact_phase(char* smem, const uint32_t (*bits)[k
 
 // ---------------------------------------------------------- routing / approx
 
-// Routing of every pooled key for both query blocks of the pair: bit j of
-// bits[g] is set iff shat_gj = scale * Qbar_g . Kbar_j >= tau_g (Eq. 4).
-// The page streams this test chunk by chunk inside the outer loop; since the
-// selected set is the union of the chunks' sets (the chunk-wise streaming
-// identity), the kernel runs the whole row up front, one pooled key per
-// thread with a float32 dot product in order of d, and the exact blocks then
-// stream back to back.  Each wave covers 64 consecutive keys, so the words it
-// writes are its own.
-template <int D, int BLK>
-__device__ __forceinline__ void route_all(uint32_t (*bits)[kMaxBlocks / 32],
-                                          const float (*qbar_s)[D], const float* kbar_h,
-                                          uint32_t N, float tau0, float tau1, float scale,
-                                          int tid, int lane) {
-  using C = Cfg<D, BLK>;
-  for (uint32_t j0 = tid - lane; j0 < N; j0 += C::NT) {
-    const uint32_t j = j0 + lane;
-    float d0 = 0.f, d1 = 0.f;
-    if (j < N) {
-      const float* kr = kbar_h + (size_t)j * D;
-#pragma unroll 8
-      for (int e = 0; e < D; e += 4) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + e);
-        const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][e]);
-        const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][e]);
+// Sum of the NV values v[] over each aligned group of G consecutive lanes
+// (NV <= G, both powers of two), by recursive halving: at each step a lane
+// keeps one half of its values and adds the partner's copy of that half, so
+// NV values need NV - 1 + log2(G / NV) exchanges instead of NV * log2(G).
+// Lane l of a group ends with the full sum of v[(l % G) / (G / NV)].
+template <int G, int NV>
+__device__ __forceinline__ float group_transpose_sum(float (&v)[NV], int lane) {
+  static_assert(NV >= 1 && NV <= G && (NV & (NV - 1)) == 0 && (G & (G - 1)) == 0, "shape");
+  int o = G / 2;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          d0 = __builtin_fmaf(q0[x], kv[x], d0);
-          d1 = __builtin_fmaf(q1[x], kv[x], d1);
-        }
-      }
-    }
-    const uint64_t b0 = __ballot(j < N && scale * d0 >= tau0);
-    const uint64_t b1 = __ballot(j < N && scale * d1 >= tau1);
-    if (lane == 0) {
-      bits[0][j0 / 32] = (uint32_t)b0;
-      bits[0][j0 / 32 + 1] = (uint32_t)(b0 >> 32);
-      bits[1][j0 / 32] = (uint32_t)b1;
-      bits[1][j0 / 32 + 1] = (uint32_t)(b1 >> 32);
+  for (int n = NV; n > 1; n /= 2, o /= 2) {
+    const bool upper = (lane & o) != 0;
+#pragma unroll
+    for (int e = 0; e < n / 2; ++e) {
+      const float send = upper ? v[e] : v[e + n / 2];
+      const float keep = upper ? v[e + n / 2] : v[e];
+      v[e] = keep + __shfl_xor(send, o);
     }
   }
+  float r = v[0];
+#pragma unroll
+  for (; o >= 1; o /= 2) r += __shfl_xor(r, o);
+  return r;
 }
 
-// One thread's share of a sub-chunk of SUB = 32 pooled rows (Kbar and Vhat,
-// float32 in global memory), held in registers between its load and its
-// bf16 store into LDS: the K rows in the K-tile layout (so score_tile reads
-// them as a 32-key tile) and the V rows in the V-tile layout (so pv_step
-// reads them as two 16-key k-steps).  Rows past the head's last block are 0.
+// One thread's share of a sub-chunk of SUB pooled rows (Kbar and Vhat,
+// float32 in global memory, read with consecutive threads on consecutive
+// 16-byte pieces of a row), held in registers between its load and its use:
+//   * the routing dot products scale * Qbar_g . Kbar_j of its rows for both
+//     query blocks (partial over its 4 d values, then summed over the row's
+//     threads), written to LDS;
+//   * the bf16 copies in the K-tile layout (so score_tile reads them as
+//     32-key tiles) and in the V-tile layout (so pv_step reads them as 16-key
+//     k-steps).
+// Rows past the head's last block are 0.
 template <int D, int BLK>
 struct PooledStage {
   using C = Cfg<D, BLK>;
-  static constexpr int Q4 = D / 4;                       // float4 per row
+  static constexpr int Q4 = D / 4;                       // float4 per row (threads per row)
   static constexpr int PER = C::SUB * Q4 / C::NT;        // float4 per thread per array
+  static constexpr int RSTRIDE = C::NT / Q4;             // rows between a thread's pieces
   static_assert(PER * C::NT == C::SUB * Q4, "sub-chunk must split evenly");
   f32x4 k[PER], v[PER];
   __device__ __forceinline__ void load(const float* kbar_h, const float* vhat_h, uint32_t jb,
                                        uint32_t N, int tid) {
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
-      const int idx = tid + c * C::NT, row = idx / Q4, q4 = idx % Q4;
+      const int row = tid / Q4 + c * RSTRIDE, q4 = tid % Q4;
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if (jb + row < N) {
         const size_t g = (size_t)(jb + row) * D + 4 * q4;
@@ -571,10 +561,31 @@ struct PooledStage {
       v[c] = vv;
     }
   }
+  // dots[g][row] = Qbar_g . Kbar_row (float32, unscaled) for the staged rows.
+  // q0 / q1: this thread's 4 d values of Qbar of the two query blocks.
+  __device__ __forceinline__ void route(float (*dots)[C::SUB], f32x4 q0, f32x4 q1, int tid,
+                                        int lane) const {
+    float part[2 * PER];
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        d0 = __builtin_fmaf(q0[x], k[c][x], d0);
+        d1 = __builtin_fmaf(q1[x], k[c][x], d1);
+      }
+      part[2 * c] = d0;
+      part[2 * c + 1] = d1;
+    }
+    const float tot = group_transpose_sum<Q4, 2 * PER>(part, lane);
+    constexpr int SPAN = Q4 / (2 * PER);  // lanes holding the same total
+    const int idx = (lane % Q4) / SPAN;   // = 2 c + g
+    if (lane % SPAN == 0) dots[idx % 2][tid / Q4 + (idx / 2) * RSTRIDE] = tot;
+  }
   __device__ __forceinline__ void store(char* kt, char* vt, int tid) const {
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
-      const int idx = tid + c * C::NT, row = idx / Q4, d = 4 * (idx % Q4);
+      const int row = tid / Q4 + c * RSTRIDE, d = 4 * (tid % Q4);
       const int byte = (d % 8) * 2;
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       auto pack4 = [](f32x4 x) {
@@ -593,86 +604,111 @@ struct PooledStage {
   }
 };
 
-// Zeroth-order terms (Eqs. 9-10) of the staged pooled keys whose bit is set
-// in unsel, for this wave's 32 queries: logits scale * q_r . Kbar_j from the
-// token-to-block tile (Eq. 11; MFMA on bf16 Kbar), denominator weight n_j,
-// numerator Vhat_j.  jb = pooled key of staged row 0.
+// Zeroth-order terms (Eqs. 9-10) of staged rows 32 half .. 32 half + 31
+// whose bit is set in unsel, for this wave's 32 queries: logits
+// scale * q_r . Kbar_j from the token-to-block tile (Eq. 11; MFMA on bf16
+// Kbar), denominator weight n_j, numerator Vhat_j.  jb = pooled key of the
+// first of those rows.
 template <int D, int BLK>
 __device__ __forceinline__ void approx_sub(const char* kt, const char* vt,
                                            const LaneOffsets<D, BLK>& off, const bf16x8* qreg,
-                                           uint32_t unsel, uint32_t jb, uint32_t N, int n_last,
-                                           float c, float& m_run, float& l_run, f32x16* o,
-                                           int lane) {
+                                           int half, uint32_t unsel, uint32_t jb, uint32_t N,
+                                           int n_last, float c, float& m_run, float& l_run,
+                                           f32x16* o, int lane) {
   using C = Cfg<D, BLK>;
   const int h = lane / 32;
-  f32x16 t = score_tile<D, BLK>(kt, off, qreg, 0);
+  f32x16 t = score_tile<D, BLK>(kt, off, qreg, half);
+  // register r of this lane holds staged row 4 h + kRow[r]; with the lane's
+  // bits pre-shifted, every test below is against a compile-time position
+  const uint32_t uh = unsel >> (4 * h);
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (!((unsel >> mfma_row(r, h)) & 1u)) t[r] = -INFINITY;
+    if (!((uh >> (8 * (r / 4) + r % 4)) & 1u)) t[r] = -INFINITY;
     mx = fmaxf(mx, t[r]);
   }
   mx = wave_max_pair(mx);
   raise_max<C::DT>(mx * c, m_run, l_run, o);
   bf16x8 pk0, pk1;
   tile_probs(t, c, m_run, &pk0, &pk1);
-  float lsum = 0.f;
+  // denominator weights n_j (on the bf16 P, as the numerator sees it): BLK
+  // for every pooled key but the head's last, which weighs n_last
+  float lsum = (float)BLK * sum_bf16x8(pk1, sum_bf16x8(pk0, 0.f));
+  const int rel = (int)(N - 1 - jb) - 4 * h;  // the last key's row, in this lane's numbering
+  if (n_last != BLK && N - 1 - jb < 32u) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    // weight n_j of the block behind pooled key jb + row (bf16 P, as the numerator)
-    const float w = (jb + mfma_row(r, h) == N - 1) ? (float)n_last : (float)BLK;
-    lsum = __builtin_fmaf(w, (float)(r < 8 ? pk0[r] : pk1[r - 8]), lsum);
+    for (int r = 0; r < 16; ++r)
+      if (rel == 8 * (r / 4) + r % 4)
+        lsum -= (float)(BLK - n_last) * (float)(r < 8 ? pk0[r] : pk1[r - 8]);
   }
-  pv_step<D, BLK>(vt, off, pk0, 0, o);
-  pv_step<D, BLK>(vt, off, pk1, 1, o);
+  pv_step<D, BLK>(vt, off, pk0, 2 * half, o);
+  pv_step<D, BLK>(vt, off, pk1, 2 * half + 1, o);
   l_run += lsum;
 }
 
-// The approximation pass over all sub-chunks of 32 pooled keys that hold an
-// unselected block of either query block, with the next sub-chunk's rows
-// loaded into registers while the current one is used (one barrier each).
-// Staging buffers: halves of the second K and V tiles.
+// The outer loop over the pooled keys, SUB = 64 at a time, for both query
+// blocks of the pair.  Per sub-chunk:
+//   * routing (Eq. 4 with the chunk-wise streaming test, Eqs. 6-7):
+//     shat_gj = scale * Qbar_g . Kbar_j >= tau_g in float32, with the dot
+//     products formed from the same coalesced float32 loads that feed the
+//     staging; the selected bits of the sub-chunk go to the group's on-chip
+//     bitmap (the page reads these scores off the token-to-block tile as
+//     column means: the same numbers, which a bf16 tile could not resolve
+//     inside the tie band);
+//   * approximation: the unselected columns of the token-to-block tile enter
+//     the group's online softmax with weight n_j and value Vhat_j (skipped in
+//     exact-only mode).
+// The next sub-chunk's rows are loaded into registers while the current one
+// is used; staging buffers alternate between the two K / V tile buffers,
+// which are free until the exact phase starts, so each sub-chunk costs one
+// workgroup barrier.  On return both groups' bitmaps are complete and the
+// tile buffers are free.
 template <int D, int BLK>
-__device__ __forceinline__ void approx_phase(char* smem, const uint32_t (*bits)[kMaxBlocks / 32],
-                                             bool pair1_on, const float* kbar_h,
-                                             const float* vhat_h, uint32_t N, int n_last,
-                                             bool grp_on, int grp, const bf16x8* qreg, float c,
-                                             float& m_run, float& l_run, f32x16* o, int tid,
-                                             int lane) {
+__device__ __forceinline__ void route_approx_phase(
+    char* smem, uint32_t (*bits)[kMaxBlocks / 32], const float (*qbar_s)[D], const float* kbar_h,
+    const float* vhat_h, uint32_t N, int n_last, float tau_g, float scale, bool approx,
+    bool grp_on, int grp, bool grp_writer, const bf16x8* qreg, float c, float& m_run,
+    float& l_run, f32x16* o, int tid, int lane) {
   using C = Cfg<D, BLK>;
-  constexpr int STAGE = C::SUB * C::ROW;  // bytes of one staged bf16 sub-chunk
-  static_assert(2 * STAGE <= C::TILE, "two staged sub-chunks must fit one tile buffer");
+  static_assert(C::SUB == 64 && C::SUB <= BLK, "a staged sub-chunk is one 64-bit word per group");
+  using Stage = PooledStage<D, BLK>;
+  auto dots = reinterpret_cast<float(*)[2][C::SUB]>(smem + C::DOTS);  // [buffer][group][row]
   const uint32_t nsub = (N + C::SUB - 1) / C::SUB;
-  auto unsel_of = [&](int g, uint32_t sb) {
-    const uint32_t rows = N - sb * C::SUB;
-    const uint32_t valid = rows >= 32 ? 0xffffffffu : ((1u << rows) - 1u);
-    return (g == 1 && !pair1_on) ? 0u : (valid & ~bits[g][sb]);
-  };
-  auto next_needed = [&](uint32_t sb) {
-    while (sb < nsub && (unsel_of(0, sb) | unsel_of(1, sb)) == 0u) ++sb;
-    return sb;
-  };
+  const int q4 = tid % Stage::Q4;
+  const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][4 * q4]);
+  const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][4 * q4]);
   LaneOffsets<D, BLK> off;
   off.init(lane);
-  PooledStage<D, BLK> st;
-  uint32_t sb = next_needed(0);
-  if (sb < nsub) st.load(kbar_h, vhat_h, sb * C::SUB, N, tid);
+  Stage st;
+  st.load(kbar_h, vhat_h, 0, N, tid);
   int buf = 0;
-  while (sb < nsub) {
-    const uint32_t nb = next_needed(sb + 1);
-    char* kt = smem + C::K1 + buf * STAGE;
-    char* vt = smem + C::V1 + buf * STAGE;
+  for (uint32_t sb = 0; sb < nsub; ++sb) {
+    char* kt = smem + (buf ? C::K1 : C::K0);
+    char* vt = smem + (buf ? C::V1 : C::V0);
+    st.route(dots[buf], q0, q1, tid, lane);
     st.store(kt, vt, tid);
-    if (nb < nsub) st.load(kbar_h, vhat_h, nb * C::SUB, N, tid);
-    __syncthreads();  // staged rows visible; the other buffer's readers are done
-    const uint32_t unsel = unsel_of(grp, sb);
-    if (grp_on && unsel)
-      approx_sub<D, BLK>(kt, vt - C::V0, off, qreg, unsel, sb * C::SUB, N, n_last, c, m_run,
-                         l_run, o, lane);
+    if (sb + 1 < nsub) st.load(kbar_h, vhat_h, (sb + 1) * C::SUB, N, tid);
+    __syncthreads();  // staged rows and dots visible; the other buffer's readers are done
+    const uint32_t j = sb * C::SUB + lane;
+    const uint64_t valid = __ballot(j < N);
+    const uint64_t sel = __ballot(j < N && scale * dots[buf][grp][lane] >= tau_g);
+    if (grp_writer && lane == 0) {
+      bits[grp][2 * sb] = (uint32_t)sel;
+      bits[grp][2 * sb + 1] = (uint32_t)(sel >> 32);
+    }
+    const uint64_t unsel = valid & ~sel;
+    if (approx && grp_on) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t u = (uint32_t)(unsel >> (32 * half));
+        if (u)
+          approx_sub<D, BLK>(kt, vt - C::V0, off, qreg, half, u, sb * C::SUB + 32 * half, N,
+                             n_last, c, m_run, l_run, o, lane);
+      }
+    }
     buf ^= 1;
-    sb = nb;
   }
-  __syncthreads();  // staging buffers free
+  __syncthreads();  // bitmaps complete; staging buffers free
 }
 
 // ------------------------------------------------------------------ kernel
@@ -681,8 +717,6 @@ template <int D, int BLK, bool FUSED>
 __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char smem[FUSED ? C::SMEM_FUSED : C::SMEM_DENSE];
-  char* const k1 = smem + C::K1;  // the routing / approximation phase stages pooled rows
-  char* const v1 = smem + C::V1;  // in the second K / V buffers
   auto selbits = reinterpret_cast<uint32_t(*)[kMaxBlocks / 32]>(smem + C::BITS);
   auto qbar_s = reinterpret_cast<float(*)[D]>(smem + C::QBAR);
 
@@ -723,10 +757,9 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
 
   if constexpr (FUSED) {
-    // ---- outer loop: routing of every pooled key, then the approximation
+    // ---- outer loop: routing and approximation, sub-chunk by sub-chunk
     const uint32_t item0 = bh * N + 2 * pair;
-    const float tau0 = a.tau[item0];
-    const float tau1 = pair1_on ? a.tau[item0 + 1] : INFINITY;
+    const float tau_g = grp_on ? a.tau[item0 + grp] : INFINITY;
     for (int cc = tid; cc < 2 * D; cc += C::NT) {
       const int gq = cc / D;
       qbar_s[gq][cc % D] =
@@ -736,12 +769,10 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
     const float* kbar_h = a.kbar + (size_t)bh * N * D;
     const float* vhat_h = a.vhat + (size_t)bh * N * D;
     __syncthreads();
-    route_all<D, BLK>(selbits, qbar_s, kbar_h, N, tau0, tau1, a.scale, tid, lane);
-    __syncthreads();  // bitmaps complete
-    if (!a.exact_only)
-      approx_phase<D, BLK>(smem, selbits, pair1_on, kbar_h, vhat_h, N,
-                           (int)(L - (int64_t)(N - 1) * BLK), grp_on, grp, qreg, a.c_log2, m_run,
-                           l_run, o, tid, lane);
+    route_approx_phase<D, BLK>(smem, selbits, qbar_s, kbar_h, vhat_h, N,
+                               (int)(L - (int64_t)(N - 1) * BLK), tau_g, a.scale, !a.exact_only,
+                               grp_on, grp, (wave % C::QW) == 0, qreg, a.c_log2, m_run, l_run, o,
+                               tid, lane);
 
     // debug outputs: the group's first wave writes its row of the bitmap
     if (grp_on && (wave % C::QW) == 0) {
