@@ -112,6 +112,109 @@ def cpu_baseline(w: synth.Workload, beta: float, heads: int = 3):
             "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def _to_device(w: synth.Workload):
+    qb, kb, vb = synth.make_inputs_bf16_bits(w)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    return dev(qb), dev(kb), dev(vb)
+
+
+def _time_ms(fn, reps: int) -> float:
+    """Mean duration of fn() over reps calls, HIP events on the current stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _errors(o: torch.Tensor, ref: torch.Tensor):
+    """Relative l2 error and cosine similarity of o against ref, per head, float32."""
+    a = o.float().flatten(2)
+    b = ref.float().flatten(2)
+    rel = (a - b).norm(dim=-1) / b.norm(dim=-1)
+    cos = (a * b).sum(-1) / (a.norm(dim=-1) * b.norm(dim=-1)).clamp_min(1e-30)
+    return rel.flatten().cpu().numpy(), cos.flatten().cpu().numpy()
+
+
+def accuracy_study(sa, w: synth.Workload, betas=(0.0, 0.5, 1.0, 1.5, 2.0, 3.0, math.inf)):
+    """Error of the Sol-Attn output against dense attention, with the
+    zeroth-order approximation of unselected blocks (full) and without it
+    (exact-only: the selected blocks alone, renormalised), and the cost of the
+    approximation at identical selections (same routing in both runs).  The
+    dense reference is solattn_dense_fwd on the same inputs (bf16 output)."""
+    q, k, v = _to_device(w)
+    B, H, L, d = q.shape
+    dense = torch.empty_like(q)
+    out = torch.empty_like(q)
+    pd = sa.problem(B, H, L, d, w.block, w.chunk, -math.inf)
+    sa.solattn_dense_fwd(pd, q, k, v, dense)
+    rows = []
+    for beta in betas:
+        row = {"beta": beta if math.isfinite(beta) else str(beta)}
+        for mode, eo in (("full", False), ("exact_only", True)):
+            p = sa.problem(B, H, L, d, w.block, w.chunk, beta, None, eo)
+            ws = sa.Workspace(p, debug=True)
+            sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
+            sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
+            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+                           ws.sel_count)
+            torch.cuda.synchronize()
+            row["density"] = float(ws.sel_count.double().mean().item()) / w.N
+            rel, cos = _errors(out, dense)
+            row[mode] = {"rel_l2_mean": float(rel.mean()), "rel_l2_max": float(rel.max()),
+                         "cosine_mean": float(cos.mean()), "cosine_min": float(cos.min()),
+                         "fwd_ms": _time_ms(lambda: sa.solattn_fwd(
+                             p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out), 5)}
+        row["approx_overhead"] = row["full"]["fwd_ms"] / row["exact_only"]["fwd_ms"] - 1.0
+        rows.append(row)
+        log(f"accuracy {row}")
+    return {"study": "accuracy", "workload": f"{w.name}: B{B} H{H} L{L} d{d} block{w.block} "
+            f"C{w.chunk}", "reference": "solattn_dense_fwd (bf16 output)", "data": "synthetic",
+            "rows": rows}
+
+
+SEQ_BETAS = (0.5, 1.0, 1.5, 2.0)
+
+
+def seq_study(sa):
+    """Speedup of the whole Sol-Attn call (pool + moments + fused) over the
+    dense kernel, across sequence length and sparsity (beta), 8 heads."""
+    rows = []
+    for L in synth.SEQ_LENGTHS:
+        w = synth.seq_workload(L)
+        q, k, v = _to_device(w)
+        B, H, _, d = q.shape
+        out = torch.empty_like(q)
+        pd = sa.problem(B, H, L, d, w.block, w.chunk, -math.inf)
+        dense_ms = _time_ms(lambda: sa.solattn_dense_fwd(pd, q, k, v, out), 2)
+        for beta in SEQ_BETAS:
+            p = sa.problem(B, H, L, d, w.block, w.chunk, beta)
+            ws = sa.Workspace(p, debug=True)
+            sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
+            sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
+            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+                           ws.sel_count)
+            torch.cuda.synchronize()
+            density = float(ws.sel_count.double().mean().item()) / w.N
+            ms = _time_ms(lambda: (sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat),
+                                   sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov,
+                                                      ws.tau),
+                                   sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau,
+                                                  out)), 3)
+            row = {"L": L, "beta": beta, "density": density, "sparsity": 1.0 - density,
+                   "ms_per_call": ms, "dense_ms": dense_ms, "speedup_vs_dense": dense_ms / ms}
+            rows.append(row)
+            log(f"seq {row}")
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    return {"study": "seq", "workload": "B1 H8 d128 block128 C32, L tokens on a (L/4096)x64x64 "
+            "grid (3D positional synthetic Q/K, N(0,1) V)", "data": "synthetic", "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +225,11 @@ def main() -> int:
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--study", choices=("accuracy", "seq"), default=None,
+                    help="instead of the headline line, print one JSON line for a study: "
+                         "'accuracy' (error against dense attention and cost of the "
+                         "approximation, full vs exact-only, over beta) or 'seq' (speedup over "
+                         "the dense kernel across sequence length and sparsity)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling "
                          "rocprofv3 byte counters) and exit")
@@ -146,6 +254,13 @@ def main() -> int:
         return 0
 
     from free_dynamic_sparse_amd import solattn as sa
+
+    if args.study == "accuracy":
+        print(json.dumps(accuracy_study(sa, synth.WORKLOADS[args.workload])), flush=True)
+        return 0
+    if args.study == "seq":
+        print(json.dumps(seq_study(sa)), flush=True)
+        return 0
 
     w = synth.WORKLOADS[args.workload]
     t0 = time.time()

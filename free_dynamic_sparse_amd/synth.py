@@ -86,6 +86,19 @@ WORKLOADS = {
 }
 
 
+# Sequence-length sweep (speedup over dense attention across length and
+# sparsity): L tokens on an (L / 4096) x 64 x 64 latent grid, 8 heads.
+SEQ_LENGTHS = (16384, 32768, 65536, 131072)
+
+
+def seq_workload(L: int, H: int = 8) -> Workload:
+    """Video-like sweep shape: L tokens on a (L / 4096, 64, 64) grid, d = 128."""
+    if L <= 0 or L % 4096:
+        raise ValueError("sweep lengths are whole 64x64 frames")
+    return Workload(f"seq{L // 1024}k", B=1, H=H, L=L, d=128, block=128, chunk=32, seed=5,
+                    kind="pos", grid=(L // 4096, 64, 64), betas=(0.5, 1.0, 1.5, 2.0))
+
+
 def _rng(*key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(x) for x in key])))
 

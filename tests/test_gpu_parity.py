@@ -239,7 +239,9 @@ def sampled_rows(N, n=6):
 
 
 def full_size(sa, name, beta, heads_checked, n_rows=6):
-    w = synth.WORKLOADS[name]
+    """name: a workload name or a synth.Workload."""
+    w = synth.WORKLOADS[name] if isinstance(name, str) else name
+    name = w.name
     t0 = time.time()
     qb, kb, vb = synth.make_inputs_bf16_bits(w)
     log(f"{name}: inputs generated in {time.time() - t0:.1f}s")
@@ -283,3 +285,11 @@ def test_hunyuan_full_size(sa):
 @pytest.mark.parametrize("beta", [-math.inf, 3.0])
 def test_stress_full_size(sa, beta):
     full_size(sa, "stress", beta, heads_checked=(0, 7), n_rows=3)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("L,beta", [(16384, 2.0), (131072, 1.0)])
+def test_seq_sweep_shapes(sa, L, beta):
+    # the sequence-length sweep's shortest and longest shapes, in the
+    # configuration the sweep times
+    full_size(sa, synth.seq_workload(L), beta, heads_checked=(0, 7), n_rows=3)
