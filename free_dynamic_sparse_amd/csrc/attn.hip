@@ -82,8 +82,7 @@ struct Cfg {
   static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
   static constexpr int BITS = 4 * TILE;                      // 2 x kMaxBlocks bits
   static constexpr int QBAR = BITS + 2 * (kMaxBlocks / 8);  // 2 x D floats
-  static constexpr int DOTS = QBAR + 2 * D * 4;              // 2 x 2 x SUB floats
-  static constexpr int SMEM_FUSED = DOTS + 2 * 2 * SUB * 4;
+  static constexpr int SMEM_FUSED = QBAR + 2 * D * 4;
   static constexpr int SMEM_DENSE = 4 * TILE;
   static_assert(DMA * WAVES * 1024 == TILE, "tile must split into whole 1 KB loads");
 };
@@ -503,37 +502,22 @@ __device__ __forceinline__ void exact_phase(char* smem, const uint32_t (*bits)[k
 
 // ---------------------------------------------------------- routing / approx
 
-// Sum of the NV values v[] over each aligned group of G consecutive lanes
-// (NV <= G, both powers of two), by recursive halving: at each step a lane
-// keeps one half of its values and adds the partner's copy of that half, so
-// NV values need NV - 1 + log2(G / NV) exchanges instead of NV * log2(G).
-// Lane l of a group ends with the full sum of v[(l % G) / (G / NV)].
-template <int G, int NV>
-__device__ __forceinline__ float group_transpose_sum(float (&v)[NV], int lane) {
-  static_assert(NV >= 1 && NV <= G && (NV & (NV - 1)) == 0 && (G & (G - 1)) == 0, "shape");
-  int o = G / 2;
-#pragma unroll
-  for (int n = NV; n > 1; n /= 2, o /= 2) {
-    const bool upper = (lane & o) != 0;
-#pragma unroll
-    for (int e = 0; e < n / 2; ++e) {
-      const float send = upper ? v[e] : v[e + n / 2];
-      const float keep = upper ? v[e + n / 2] : v[e];
-      v[e] = keep + __shfl_xor(send, o);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (; o >= 1; o /= 2) r += __shfl_xor(r, o);
-  return r;
+// x from lane l's partner under a DPP lane permutation within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]: lane i <-> i ^ 1
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]: lane i <-> i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7 - i within 8 lanes
 
 // One thread's share of a sub-chunk of SUB pooled rows (Kbar and Vhat,
-// float32 in global memory, read with consecutive threads on consecutive
-// 16-byte pieces of a row), held in registers between its load and its use:
-//   * the routing dot products scale * Qbar_g . Kbar_j of its rows for both
-//     query blocks (partial over its 4 d values, then summed over the row's
-//     threads), written to LDS;
+// float32 in global memory), held in registers between its load and its use:
+// TPR consecutive threads share a row, thread q of them holding the float4
+// pieces q, q + TPR, q + 2 TPR, ... of it (so each load instruction reads
+// whole 128-byte lines).  From these registers come
+//   * the routing decisions of the staged rows for both query blocks, and
 //   * the bf16 copies in the K-tile layout (so score_tile reads them as
 //     32-key tiles) and in the V-tile layout (so pv_step reads them as 16-key
 //     k-steps).
@@ -541,19 +525,21 @@ __device__ __forceinline__ float group_transpose_sum(float (&v)[NV], int lane) {
 template <int D, int BLK>
 struct PooledStage {
   using C = Cfg<D, BLK>;
-  static constexpr int Q4 = D / 4;                       // float4 per row (threads per row)
-  static constexpr int PER = C::SUB * Q4 / C::NT;        // float4 per thread per array
-  static constexpr int RSTRIDE = C::NT / Q4;             // rows between a thread's pieces
-  static_assert(PER * C::NT == C::SUB * Q4, "sub-chunk must split evenly");
-  f32x4 k[PER], v[PER];
+  static constexpr int E = D * C::SUB / C::NT;  // elements of one row per thread
+  static constexpr int F4 = E / 4;              // float4 pieces per thread per array
+  static constexpr int TPR = D / E;             // threads per row
+  static constexpr int RPW = kWave / TPR;       // rows per wave
+  static_assert(TPR == 4 || TPR == 8, "routing reduction covers 4 or 8 lanes");
+  static_assert(F4 * 4 == E && TPR * C::SUB == C::NT, "sub-chunk must split evenly");
+  f32x4 k[F4], v[F4];
   __device__ __forceinline__ void load(const float* kbar_h, const float* vhat_h, uint32_t jb,
                                        uint32_t N, int tid) {
+    const int row = tid / TPR, q = tid % TPR;
 #pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      const int row = tid / Q4 + c * RSTRIDE, q4 = tid % Q4;
+    for (int c = 0; c < F4; ++c) {
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if (jb + row < N) {
-        const size_t g = (size_t)(jb + row) * D + 4 * q4;
+        const size_t g = (size_t)(jb + row) * D + 4 * (q + TPR * c);
         kk = *reinterpret_cast<const f32x4*>(kbar_h + g);
         vv = *reinterpret_cast<const f32x4*>(vhat_h + g);
       }
@@ -561,31 +547,60 @@ struct PooledStage {
       v[c] = vv;
     }
   }
-  // dots[g][row] = Qbar_g . Kbar_row (float32, unscaled) for the staged rows.
-  // q0 / q1: this thread's 4 d values of Qbar of the two query blocks.
-  __device__ __forceinline__ void route(float (*dots)[C::SUB], f32x4 q0, f32x4 q1, int tid,
-                                        int lane) const {
-    float part[2 * PER];
+  // Routing (Eq. 4) of the staged rows jb .. jb + SUB - 1: row j is selected
+  // for group g iff scale * Qbar_g . Kbar_j >= tau_g, with the dot product in
+  // float32 (each thread's pieces, then summed over the row's TPR lanes).
+  // The wave's RPW rows give RPW bits per group, written to the groups'
+  // bitmaps (bits viewed as bytes; sub-chunk sb = bytes 8 sb .. 8 sb + 7).
+  __device__ __forceinline__ void route(uint8_t* bits0, uint8_t* bits1, const float (*qbar_s)[D],
+                                        float tau0, float tau1, float scale, uint32_t jb,
+                                        uint32_t N, int tid, int lane, int wave) const {
+    const int q = tid % TPR;
+    float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      float d0 = 0.f, d1 = 0.f;
+    for (int c = 0; c < F4; ++c) {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][4 * (q + TPR * c)]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][4 * (q + TPR * c)]);
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        d0 = __builtin_fmaf(q0[x], k[c][x], d0);
-        d1 = __builtin_fmaf(q1[x], k[c][x], d1);
+        d0 = __builtin_fmaf(a0[x], k[c][x], d0);
+        d1 = __builtin_fmaf(a1[x], k[c][x], d1);
       }
-      part[2 * c] = d0;
-      part[2 * c + 1] = d1;
     }
-    const float tot = group_transpose_sum<Q4, 2 * PER>(part, lane);
-    constexpr int SPAN = Q4 / (2 * PER);  // lanes holding the same total
-    const int idx = (lane % Q4) / SPAN;   // = 2 c + g
-    if (lane % SPAN == 0) dots[idx % 2][tid / Q4 + (idx / 2) * RSTRIDE] = tot;
+    // Sum over the row's lanes: the first exchange pairs each lane of the
+    // lower half with one of the upper half; the lower half keeps group 0's
+    // partial sums and the upper half group 1's, so one exchange serves both.
+    const bool upper = (lane & (TPR / 2)) != 0;
+    const float send = upper ? d0 : d1;
+    float t = upper ? d1 : d0;
+    t += (TPR == 8) ? dpp_move<kDppHalfMirror>(send) : dpp_move<kDppQuadXor2>(send);
+    if (TPR == 8) t += dpp_move<kDppQuadXor2>(t);
+    t += dpp_move<kDppQuadXor1>(t);
+    const uint32_t j = jb + (uint32_t)(tid / TPR);
+    const uint64_t b = __ballot(j < N && scale * t >= (upper ? tau1 : tau0));
+    // row rr of the wave: group 0 in lane TPR rr, group 1 in lane TPR rr + TPR / 2
+    uint32_t s0 = 0u, s1 = 0u;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      s0 |= (uint32_t)((b >> (TPR * rr)) & 1u) << rr;
+      s1 |= (uint32_t)((b >> (TPR * rr + TPR / 2)) & 1u) << rr;
+    }
+    if (lane == 0) {
+      const uint32_t byte = (jb / 8) + (uint32_t)wave * (RPW / 8);
+      if (RPW == 8) {
+        bits0[byte] = (uint8_t)s0;
+        bits1[byte] = (uint8_t)s1;
+      } else {
+        *reinterpret_cast<uint16_t*>(bits0 + byte) = (uint16_t)s0;
+        *reinterpret_cast<uint16_t*>(bits1 + byte) = (uint16_t)s1;
+      }
+    }
   }
   __device__ __forceinline__ void store(char* kt, char* vt, int tid) const {
+    const int row = tid / TPR, q = tid % TPR;
 #pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      const int row = tid / Q4 + c * RSTRIDE, d = 4 * (tid % Q4);
+    for (int c = 0; c < F4; ++c) {
+      const int d = 4 * (q + TPR * c);
       const int byte = (d % 8) * 2;
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       auto pack4 = [](f32x4 x) {
@@ -666,17 +681,15 @@ __device__ __forceinline__ void approx_sub(const char* kt, const char* vt,
 template <int D, int BLK>
 __device__ __forceinline__ void route_approx_phase(
     char* smem, uint32_t (*bits)[kMaxBlocks / 32], const float (*qbar_s)[D], const float* kbar_h,
-    const float* vhat_h, uint32_t N, int n_last, float tau_g, float scale, bool approx,
-    bool grp_on, int grp, bool grp_writer, const bf16x8* qreg, float c, float& m_run,
-    float& l_run, f32x16* o, int tid, int lane) {
+    const float* vhat_h, uint32_t N, int n_last, float tau0, float tau1, float scale,
+    bool approx, bool grp_on, int grp, const bf16x8* qreg, float c, float& m_run, float& l_run,
+    f32x16* o, int tid, int wave, int lane) {
   using C = Cfg<D, BLK>;
   static_assert(C::SUB == 64 && C::SUB <= BLK, "a staged sub-chunk is one 64-bit word per group");
   using Stage = PooledStage<D, BLK>;
-  auto dots = reinterpret_cast<float(*)[2][C::SUB]>(smem + C::DOTS);  // [buffer][group][row]
   const uint32_t nsub = (N + C::SUB - 1) / C::SUB;
-  const int q4 = tid % Stage::Q4;
-  const f32x4 q0 = *reinterpret_cast<const f32x4*>(&qbar_s[0][4 * q4]);
-  const f32x4 q1 = *reinterpret_cast<const f32x4*>(&qbar_s[1][4 * q4]);
+  uint8_t* const bits0 = reinterpret_cast<uint8_t*>(bits[0]);
+  uint8_t* const bits1 = reinterpret_cast<uint8_t*>(bits[1]);
   LaneOffsets<D, BLK> off;
   off.init(lane);
   Stage st;
@@ -685,19 +698,16 @@ __device__ __forceinline__ void route_approx_phase(
   for (uint32_t sb = 0; sb < nsub; ++sb) {
     char* kt = smem + (buf ? C::K1 : C::K0);
     char* vt = smem + (buf ? C::V1 : C::V0);
-    st.route(dots[buf], q0, q1, tid, lane);
+    st.route(bits0, bits1, qbar_s, tau0, tau1, scale, sb * C::SUB, N, tid, lane, wave);
     st.store(kt, vt, tid);
     if (sb + 1 < nsub) st.load(kbar_h, vhat_h, (sb + 1) * C::SUB, N, tid);
-    __syncthreads();  // staged rows and dots visible; the other buffer's readers are done
-    const uint32_t j = sb * C::SUB + lane;
-    const uint64_t valid = __ballot(j < N);
-    const uint64_t sel = __ballot(j < N && scale * dots[buf][grp][lane] >= tau_g);
-    if (grp_writer && lane == 0) {
-      bits[grp][2 * sb] = (uint32_t)sel;
-      bits[grp][2 * sb + 1] = (uint32_t)(sel >> 32);
-    }
-    const uint64_t unsel = valid & ~sel;
+    __syncthreads();  // staged rows and their bits visible; the other buffer's readers are done
     if (approx && grp_on) {
+      const uint32_t rem = N - sb * C::SUB;
+      const uint64_t valid = rem >= 64u ? ~0ull : ((1ull << rem) - 1ull);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(bits[grp][2 * sb]);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(bits[grp][2 * sb + 1]);
+      const uint64_t unsel = valid & ~(((uint64_t)hi << 32) | lo);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const uint32_t u = (uint32_t)(unsel >> (32 * half));
@@ -759,7 +769,8 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   if constexpr (FUSED) {
     // ---- outer loop: routing and approximation, sub-chunk by sub-chunk
     const uint32_t item0 = bh * N + 2 * pair;
-    const float tau_g = grp_on ? a.tau[item0 + grp] : INFINITY;
+    const float tau0 = a.tau[item0];
+    const float tau1 = pair1_on ? a.tau[item0 + 1] : INFINITY;
     for (int cc = tid; cc < 2 * D; cc += C::NT) {
       const int gq = cc / D;
       qbar_s[gq][cc % D] =
@@ -770,9 +781,9 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
     const float* vhat_h = a.vhat + (size_t)bh * N * D;
     __syncthreads();
     route_approx_phase<D, BLK>(smem, selbits, qbar_s, kbar_h, vhat_h, N,
-                               (int)(L - (int64_t)(N - 1) * BLK), tau_g, a.scale, !a.exact_only,
-                               grp_on, grp, (wave % C::QW) == 0, qreg, a.c_log2, m_run, l_run, o,
-                               tid, lane);
+                               (int)(L - (int64_t)(N - 1) * BLK), tau0, tau1, a.scale,
+                               !a.exact_only, grp_on, grp, qreg, a.c_log2, m_run, l_run, o, tid,
+                               wave, lane);
 
     // debug outputs: the group's first wave writes its row of the bitmap
     if (grp_on && (wave % C::QW) == 0) {
