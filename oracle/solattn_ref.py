@@ -33,6 +33,12 @@ Pins (tests/test_oracle_*.py, CPU only):
   forward_streaming    equals forward for every chunk size (C-invariance)
   dense                torch SDPA
   approx denominator   Jensen bound against the exact block denominator
+  select_topk          k largest by construction (count, order and tie
+                       invariants); with per-row counts |S_i| it reproduces
+                       threshold routing, whose sets are upper sets of the row
+  select_topp          mass reaches p and the prefix is the shortest such
+                       (invariants); uniform rows keep ceil(p N) blocks, a
+                       dominant score keeps one, p = 1 keeps the row
 No function here is "parity unpinned".
 """
 
@@ -159,6 +165,74 @@ def select(shat: np.ndarray, tau: np.ndarray) -> np.ndarray:
     GPU kernel decides in, on values computed here in float64.
     """
     return shat.astype(np.float32) >= tau.astype(np.float32)[:, None]
+
+
+# --------------------------------------------------------------------------
+# Routing baselines the page compares threshold routing with: top-k and
+# top-p over the materialised proxy map (the discussion after Eq. 4; the
+# selection-latency comparison of Figure 5(b); the density spread of
+# Figure 7).  They are not part of the method.
+# --------------------------------------------------------------------------
+
+def order_row(shat_row: np.ndarray) -> np.ndarray:
+    """Block indices of one proxy row, largest score first.
+
+    Reading: the page gives no tie rule; equal scores are taken in
+    increasing block index.
+    """
+    n = len(shat_row)
+    return np.lexsort((np.arange(n), -np.asarray(shat_row, F64)))
+
+
+def select_topk(shat: np.ndarray, k) -> np.ndarray:
+    """Top-k routing: S_i = the k_i largest entries of proxy row i.
+
+    k is one count for every row or an array of per-row counts; counts of N
+    or more select the whole row.  Every row keeps the same number of blocks
+    (a fixed budget, the contrast the page draws with threshold routing).
+    """
+    n_rows, N = shat.shape
+    ks = np.broadcast_to(np.asarray(k, dtype=np.int64), (n_rows,))
+    sel = np.zeros((n_rows, N), dtype=bool)
+    for i in range(n_rows):
+        kk = int(min(max(ks[i], 0), N))
+        sel[i, order_row(shat[i])[:kk]] = True
+    return sel
+
+
+def select_topp(shat: np.ndarray, p: float) -> np.ndarray:
+    """Top-p routing: the shortest run of a row's largest scores whose
+    softmax mass reaches p (at least one block).
+
+    Row i is sorted by score, largest first; its softmax distribution over
+    the N blocks is w_j = exp(shat_ij) / sum_l exp(shat_il); S_i is the
+    smallest prefix of the sorted order with sum_{j in prefix} w_j >= p.
+    Reading: the softmax is over the proxy logits themselves, one term per
+    block (not weighted by the block's token count), the plainest reading of
+    the cumulative mass of the softmax-score distribution; 0 < p <= 1.
+    """
+    if not 0.0 < p <= 1.0:
+        raise ValueError("top-p needs 0 < p <= 1")
+    n_rows, N = shat.shape
+    sel = np.zeros((n_rows, N), dtype=bool)
+    for i in range(n_rows):
+        o = order_row(shat[i])
+        row = np.asarray(shat[i], F64)[o]
+        w = np.exp(row - row[0])
+        cum = np.cumsum(w)
+        frac = cum / cum[-1]
+        # p = 1 is reached only by the whole row (every w_j > 0 in exact
+        # arithmetic), however small the tail's mass is in floating point
+        count = N if p >= 1.0 else min(int(np.searchsorted(frac, p, side="left")) + 1, N)
+        sel[i, o[:count]] = True
+    return sel
+
+
+def topp_mass(shat_row: np.ndarray, sel_row: np.ndarray) -> float:
+    """Softmax mass of the selected entries of one proxy row."""
+    x = np.asarray(shat_row, F64)
+    w = np.exp(x - x.max())
+    return float(w[sel_row].sum() / w.sum())
 
 
 def select_streaming(q: np.ndarray, kbar: np.ndarray, tau: np.ndarray,

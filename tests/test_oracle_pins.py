@@ -250,3 +250,74 @@ def test_exact_only_with_nothing_selected_outputs_zero():
     r = ref.solattn_head(q, k, v, math.inf, 64, exact_only=True)
     assert not r.sel.any()
     assert np.all(r.out == 0.0)
+
+
+# ---------------------------------------------------------------- routing baselines
+# top-k and top-p over the materialised proxy map: the baselines the page
+# compares threshold routing with.
+
+def _rows(seed, n_rows=12, N=37):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((n_rows, N)) * rng.uniform(0.2, 3.0, (n_rows, 1))
+
+
+@pytest.mark.parametrize("k", [1, 5, 36, 37, 50])
+def test_topk_keeps_the_k_largest(k):
+    shat = _rows(1)
+    sel = ref.select_topk(shat, k)
+    N = shat.shape[1]
+    for i in range(shat.shape[0]):
+        assert sel[i].sum() == min(k, N)
+        if 0 < sel[i].sum() < N:
+            assert shat[i][sel[i]].min() >= shat[i][~sel[i]].max()
+
+
+def test_topk_breaks_ties_by_block_index():
+    row = np.array([[1.0, 3.0, 2.0, 3.0, 2.0, 2.0, 0.0]])
+    assert np.array_equal(np.flatnonzero(ref.select_topk(row, 3)[0]), [1, 2, 3])
+    assert np.array_equal(np.flatnonzero(ref.select_topk(row, 4)[0]), [1, 2, 3, 4])
+
+
+@pytest.mark.parametrize("beta", [-0.5, 0.5, 1.0, 2.0])
+def test_topk_with_threshold_counts_is_threshold_routing(beta):
+    # S_i = {j : shat_ij >= tau_i} is an upper set of row i, so the top-|S_i|
+    # entries of the row are exactly S_i
+    w = synth.Workload("pin_topk", B=1, H=1, L=64 * 40, d=64, block=64, chunk=8, seed=31,
+                       kind="pos", grid=(1, 40, 64))
+    q, k, v = synth.make_head(w, 0, 0)
+    r = ref.solattn_head(q, k, v, beta, w.block, rows=[])
+    got = ref.select_topk(r.shat, r.sel.sum(axis=1))
+    assert np.array_equal(got, r.sel)
+
+
+@pytest.mark.parametrize("p", [0.05, 0.3, 0.5, 0.9, 0.999])
+def test_topp_is_the_shortest_prefix_reaching_p(p):
+    shat = _rows(2)
+    sel = ref.select_topp(shat, p)
+    for i in range(shat.shape[0]):
+        o = ref.order_row(shat[i])
+        cnt = int(sel[i].sum())
+        assert cnt >= 1 and sel[i][o[:cnt]].all()  # a prefix of the sorted order
+        assert ref.topp_mass(shat[i], sel[i]) >= p - 1e-12
+        if cnt > 1:
+            shorter = sel[i].copy()
+            shorter[o[cnt - 1]] = False
+            assert ref.topp_mass(shat[i], shorter) < p
+
+
+@pytest.mark.parametrize("p,N", [(0.3, 37), (0.62, 20), (0.999, 11)])
+def test_topp_on_a_uniform_row_keeps_ceil_pN(p, N):
+    # equal logits: every block has mass 1/N, so the shortest prefix with mass
+    # >= p has ceil(p N) blocks (p N is not an integer here)
+    sel = ref.select_topp(np.zeros((1, N)), p)
+    assert sel.sum() == math.ceil(p * N)
+    assert np.array_equal(np.flatnonzero(sel[0]), np.arange(math.ceil(p * N)))
+
+
+def test_topp_special_cases():
+    row = np.zeros((1, 16))
+    row[0, 9] = 50.0  # one dominant logit holds mass 1 - 15 e^-50
+    assert np.array_equal(np.flatnonzero(ref.select_topp(row, 0.9)[0]), [9])
+    assert ref.select_topp(_rows(3), 1.0).all()
+    with pytest.raises(ValueError):
+        ref.select_topp(row, 0.0)
