@@ -215,6 +215,87 @@ def seq_study(sa):
             "grid (3D positional synthetic Q/K, N(0,1) V)", "data": "synthetic", "rows": rows}
 
 
+def _spread(density_rows: np.ndarray):
+    d = density_rows.ravel()
+    return {"mean": float(d.mean()), "p10": float(np.percentile(d, 10)),
+            "p90": float(np.percentile(d, 90)), "std": float(d.std())}
+
+
+def routing_study(sa, w: synth.Workload, beta: float):
+    """Threshold routing against the top-k and top-p baselines at the same mean
+    density: selection latency (routing work only, after pooling), the
+    intermediate memory it needs, and the spread of per-query-block densities.
+
+    Threshold routing: its work outside the fused kernel is the moments and
+    thresholds (solattn_moments); inside the kernel each pooled score is
+    tested on chip, a pass measured alone (exact-only at beta = +inf: it also
+    reads Q and writes O) as an upper bound.  Top-k / top-p: the proxy map
+    plus the per-row selection; k = the threshold router's mean count, p found
+    by bisection to give the same mean density."""
+    q, k, v = _to_device(w)
+    B, H, L, d = q.shape
+    N = w.N
+    out = torch.empty_like(q)
+    p = sa.problem(B, H, L, d, w.block, w.chunk, beta)
+    ws = sa.Workspace(p, debug=True)
+    sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
+    sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
+    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask, ws.sel_count)
+    torch.cuda.synchronize()
+    dens_thr = ws.sel_count.double().cpu().numpy() / N
+    rho = float(dens_thr.mean())
+    t_moments = _time_ms(lambda: sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov,
+                                                    ws.tau), 10)
+    p_inf = sa.problem(B, H, L, d, w.block, w.chunk, math.inf, None, True)
+    ws_inf = sa.Workspace(p_inf)
+    sa.solattn_moments(p_inf, ws.qbar, ws.kbar, ws_inf.kmean, ws_inf.kcov, ws_inf.tau)
+    t_pass = _time_ms(lambda: sa.solattn_fwd(p_inf, q, k, v, ws.qbar, ws.kbar, ws.vhat,
+                                             ws_inf.tau, out), 5)
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+    shat = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, H, N, (N + 63) // 64), dtype=torch.int64, device="cuda")
+    cnt = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    t_map = _time_ms(lambda: sa.solattn_proxy_map(p, ws.qbar, ws.kbar, shat), 10)
+    kk = max(1, int(round(rho * N)))
+    t_topk = _time_ms(lambda: sa.solattn_select_topk(p, shat, kk, mask, cnt), 10)
+    dens_topk = cnt.double().cpu().numpy() / N
+
+    def topp_density(pp):
+        sa.solattn_select_topp(p, shat, pp, mask, cnt)
+        return float(cnt.double().mean().item()) / N
+
+    lo, hi = 1e-6, 1.0
+    for _ in range(30):
+        mid = 0.5 * (lo + hi)
+        if topp_density(mid) < rho:
+            lo = mid
+        else:
+            hi = mid
+    top_p = hi
+    t_topp = _time_ms(lambda: sa.solattn_select_topp(p, shat, top_p, mask, cnt), 10)
+    dens_topp = cnt.double().cpu().numpy() / N
+
+    f32 = 4
+    mem_thr = B * H * (d + d * d + N) * f32  # m, Sigma, tau
+    mem_map = B * H * N * N * f32 + B * H * N * ((N + 63) // 64) * 8  # map + masks
+    ours = t_moments
+    rows = {
+        "threshold": {"beta": beta, "routing_ms": ours, "in_kernel_pass_ms_upper": t_pass,
+                      "memory_bytes": mem_thr, "density": _spread(dens_thr)},
+        "top_k": {"k": kk, "routing_ms": t_map + t_topk, "map_ms": t_map, "select_ms": t_topk,
+                  "memory_bytes": mem_map, "density": _spread(dens_topk),
+                  "slowdown_vs_threshold": (t_map + t_topk) / ours},
+        "top_p": {"p": top_p, "routing_ms": t_map + t_topp, "map_ms": t_map, "select_ms": t_topp,
+                  "memory_bytes": mem_map, "density": _spread(dens_topp),
+                  "slowdown_vs_threshold": (t_map + t_topp) / ours},
+    }
+    log(f"routing {rows}")
+    return {"study": "routing", "workload": f"{w.name}: B{B} H{H} L{L} d{d} block{w.block} "
+            f"C{w.chunk} beta{beta}", "data": "synthetic", "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,11 +306,13 @@ def main() -> int:
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--study", choices=("accuracy", "seq"), default=None,
+    ap.add_argument("--study", choices=("accuracy", "seq", "routing"), default=None,
                     help="instead of the headline line, print one JSON line for a study: "
                          "'accuracy' (error against dense attention and cost of the "
-                         "approximation, full vs exact-only, over beta) or 'seq' (speedup over "
-                         "the dense kernel across sequence length and sparsity)")
+                         "approximation, full vs exact-only, over beta), 'seq' (speedup over "
+                         "the dense kernel across sequence length and sparsity) or 'routing' "
+                         "(selection latency, memory and per-row density spread of threshold "
+                         "routing against top-k and top-p over the proxy map)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling "
                          "rocprofv3 byte counters) and exit")
@@ -260,6 +343,10 @@ def main() -> int:
         return 0
     if args.study == "seq":
         print(json.dumps(seq_study(sa)), flush=True)
+        return 0
+    if args.study == "routing":
+        print(json.dumps(routing_study(sa, synth.WORKLOADS[args.workload], args.beta)),
+              flush=True)
         return 0
 
     w = synth.WORKLOADS[args.workload]

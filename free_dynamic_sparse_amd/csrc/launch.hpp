@@ -35,4 +35,17 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
 hipError_t launch_dense(const Shape& s, const void* q, const void* k, const void* v, void* out,
                         hipStream_t stream);
 
+// Routing baselines over the materialised proxy map.
+int64_t select_max_blocks();                      // largest N a proxy row may have
+int64_t proxy_map_workgroups(const Shape& s);     // grid size of launch_proxy_map
+
+hipError_t launch_proxy_map(const Shape& s, const float* qbar, const float* kbar, float* shat,
+                            hipStream_t stream);
+
+hipError_t launch_select_topk(const Shape& s, const float* shat, int64_t k, uint64_t* sel_mask,
+                              int32_t* sel_count, hipStream_t stream);
+
+hipError_t launch_select_topp(const Shape& s, const float* shat, float top_p,
+                              uint64_t* sel_mask, int32_t* sel_count, hipStream_t stream);
+
 }  // namespace solattn

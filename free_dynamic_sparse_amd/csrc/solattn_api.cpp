@@ -115,15 +115,58 @@ int solattn_dense_fwd(const solattn_problem_t* p, const void* q, const void* k, 
   return from_hip(solattn::launch_dense(s, q, k, v, out, static_cast<hipStream_t>(stream)));
 }
 
+int solattn_proxy_map(const solattn_problem_t* p, const float* qbar, const float* kbar,
+                      float* shat, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (empty) return SOLATTN_OK;
+  if (solattn::proxy_map_workgroups(s) > kMaxGrid) return SOLATTN_E_INVALID_ARG;
+  if (!ok_ptr(qbar) || !ok_ptr(kbar) || !ok_ptr(shat)) return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_proxy_map(s, qbar, kbar, shat,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int solattn_select_topk(const solattn_problem_t* p, const float* shat, int64_t k,
+                        uint64_t* sel_mask, int32_t* sel_count, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (k < 1) return SOLATTN_E_INVALID_ARG;
+  if (s.N > solattn::select_max_blocks()) return SOLATTN_E_UNSUPPORTED;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(shat) || !ok_ptr(sel_mask) || !ok_opt_ptr(sel_count)) return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_select_topk(s, shat, k, sel_mask, sel_count,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int solattn_select_topp(const solattn_problem_t* p, const float* shat, float top_p,
+                        uint64_t* sel_mask, int32_t* sel_count, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (!(top_p > 0.f && top_p <= 1.f)) return SOLATTN_E_INVALID_ARG;
+  if (s.N > solattn::select_max_blocks()) return SOLATTN_E_UNSUPPORTED;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(shat) || !ok_ptr(sel_mask) || !ok_opt_ptr(sel_count)) return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_select_topp(s, shat, top_p, sel_mask, sel_count,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char* solattn_strerror(int code) {
   switch (code) {
     case SOLATTN_OK:
       return "ok";
     case SOLATTN_E_INVALID_ARG:
-      return "invalid argument (null or misaligned pointer, bad shape, NaN beta or scale)";
+      return "invalid argument (null or misaligned pointer, bad shape, NaN beta or scale, "
+             "k < 1, top_p outside (0, 1])";
     case SOLATTN_E_UNSUPPORTED:
       return "unsupported configuration (head_dim and block must be 64 or 128, chunk 1..64, "
-             "and solattn_fwd needs ceil(seq_len / block) <= 8192)";
+             "and solattn_fwd and the top-k / top-p selections need ceil(seq_len / block) "
+             "<= 8192)";
     case SOLATTN_E_HIP:
       return "HIP launch failed";
     default:

@@ -25,6 +25,7 @@ SOLATTN_E_HIP = -3
 SOLATTN_FLAG_EXACT_ONLY = 1
 
 EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd",
+           "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp",
            "solattn_strerror", "solattn_version")
 
 
@@ -55,7 +56,11 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.solattn_moments.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_dense_fwd.argtypes = [pp, vp, vp, vp, vp, vp]
-    for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd"):
+    lib.solattn_proxy_map.argtypes = [pp, vp, vp, vp, vp]
+    lib.solattn_select_topk.argtypes = [pp, vp, ctypes.c_int64, vp, vp, vp]
+    lib.solattn_select_topp.argtypes = [pp, vp, ctypes.c_float, vp, vp, vp]
+    for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd",
+                 "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp"):
         getattr(lib, name).restype = ctypes.c_int
     lib.solattn_strerror.argtypes = [ctypes.c_int]
     lib.solattn_strerror.restype = ctypes.c_char_p
@@ -161,6 +166,36 @@ def solattn_dense_fwd(p: Problem, q, k, v, out, stream=None) -> None:
         _need(t, torch.bfloat16, full, n)
     _check(LIB.solattn_dense_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                  _stream(stream)), "solattn_dense_fwd")
+
+
+def solattn_proxy_map(p: Problem, qbar, kbar, shat, stream=None) -> None:
+    _, pooled, N = _dims(p)
+    _need(qbar, torch.float32, pooled, "qbar")
+    _need(kbar, torch.float32, pooled, "kbar")
+    _need(shat, torch.float32, (p.batch, p.heads, N, N), "shat")
+    _check(LIB.solattn_proxy_map(ctypes.byref(p), _ptr(qbar), _ptr(kbar), _ptr(shat),
+                                 _stream(stream)), "solattn_proxy_map")
+
+
+def _select_outputs(p: Problem, shat, sel_mask, sel_count):
+    N = num_blocks(p.seq_len, p.block)
+    _need(shat, torch.float32, (p.batch, p.heads, N, N), "shat")
+    _need(sel_mask, torch.int64, (p.batch, p.heads, N, (N + 63) // 64), "sel_mask")
+    if sel_count is not None:
+        _need(sel_count, torch.int32, (p.batch, p.heads, N), "sel_count")
+
+
+def solattn_select_topk(p: Problem, shat, k: int, sel_mask, sel_count=None, stream=None) -> None:
+    _select_outputs(p, shat, sel_mask, sel_count)
+    _check(LIB.solattn_select_topk(ctypes.byref(p), _ptr(shat), int(k), _ptr(sel_mask),
+                                   _ptr(sel_count), _stream(stream)), "solattn_select_topk")
+
+
+def solattn_select_topp(p: Problem, shat, top_p: float, sel_mask, sel_count=None,
+                        stream=None) -> None:
+    _select_outputs(p, shat, sel_mask, sel_count)
+    _check(LIB.solattn_select_topp(ctypes.byref(p), _ptr(shat), float(top_p), _ptr(sel_mask),
+                                   _ptr(sel_count), _stream(stream)), "solattn_select_topp")
 
 
 class Workspace:

@@ -8,7 +8,9 @@
  *   solattn_moments  -> pooled-key moments and per-query-block thresholds tau
  *   solattn_fwd      -> the fused nested-loop attention kernel
  * and solattn_dense_fwd is plain dense softmax attention on the same core,
- * kept as the in-house comparison point.
+ * kept as the in-house comparison point.  solattn_proxy_map with
+ * solattn_select_topk / solattn_select_topp are the top-k and top-p routing
+ * baselines the page compares its routing with.
  *
  * Conventions shared by every entry point
  * - Tensors are contiguous row-major device memory.  Q, K, V and O are
@@ -143,6 +145,44 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
  */
 int solattn_dense_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
                       void* out, void* stream);
+
+/*
+ * Routing baselines the page compares threshold routing with (method section
+ * after Eq. 4; the selection-latency comparison of Figure 5(b) and the
+ * density spread of Figure 7).  Not part of the Sol-Attn forward: they
+ * materialise the N x N proxy map that the method never builds.
+ *
+ * solattn_proxy_map: shat_ij = scale * Qbar_i . Kbar_j (Eq. 3) for every
+ * query block i and key block j of each (b, h).
+ *   qbar, kbar in:  f32 [B, H, N, d]  from solattn_pool
+ *   shat       out: f32 [B, H, N, N]
+ * Float32 dot products in order of d.  beta, chunk and flags are ignored.
+ * B*H*ceil(N/64)^2 must stay below 2^31.
+ */
+int solattn_proxy_map(const solattn_problem_t* p, const float* qbar, const float* kbar,
+                      float* shat, void* stream);
+
+/*
+ * solattn_select_topk: top-k routing, S_i = the k largest entries of proxy
+ * row i (all N when k >= N); equal scores are taken in increasing block
+ * index.  solattn_select_topp: top-p routing, S_i = the shortest run of row
+ * i's largest entries (same order) whose softmax mass reaches top_p, with
+ * weights w_j = exp(shat_ij) / sum_l exp(shat_il) over the row's N blocks,
+ * at least one block; top_p = 1 selects the whole row.  Cumulative sums are
+ * float32 over the sorted row.
+ *   shat       in:  f32 [B, H, N, N]  from solattn_proxy_map
+ *   k          >= 1 (else SOLATTN_E_INVALID_ARG)
+ *   top_p      in (0, 1] (else SOLATTN_E_INVALID_ARG; NaN included)
+ *   sel_mask   out: u64 [B, H, N, ceil(N/64)], the same bitmap layout as
+ *              solattn_fwd's sel_mask
+ *   sel_count  out, may be NULL: i32 [B, H, N], |S_i|
+ * Limit: N <= 8192 (a row is sorted in on-chip memory); larger N returns
+ * SOLATTN_E_UNSUPPORTED.
+ */
+int solattn_select_topk(const solattn_problem_t* p, const float* shat, int64_t k,
+                        uint64_t* sel_mask, int32_t* sel_count, void* stream);
+int solattn_select_topp(const solattn_problem_t* p, const float* shat, float top_p,
+                        uint64_t* sel_mask, int32_t* sel_count, void* stream);
 
 /* Static text for a return code. */
 const char* solattn_strerror(int code);

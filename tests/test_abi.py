@@ -132,3 +132,32 @@ def test_moments_and_pool_reject_bad_pointers(sa):
     assert sa.LIB.solattn_moments(ctypes.byref(p), f, f, f, f, f, bad, None, None) == -1
     p.beta = math.nan
     assert sa.LIB.solattn_moments(ctypes.byref(p), f, f, f, f, f, None, None, None) == -1
+
+
+# ------------------------------------------------------------ routing baselines
+
+def test_baseline_entry_points_reject_bad_arguments(sa):
+    p = sa.problem(1, 2, 4096, 128, 128, 32, 1.0)
+    P = lambda x: ctypes.c_void_p(x)
+    lib = sa.LIB
+    # proxy map: null / misaligned pointers
+    assert lib.solattn_proxy_map(ctypes.byref(p), None, P(FAKE), P(FAKE), None) == -1
+    assert lib.solattn_proxy_map(ctypes.byref(p), P(FAKE), P(FAKE + 4), P(FAKE), None) == -1
+    # top-k: k < 1, null mask, misaligned count
+    assert lib.solattn_select_topk(ctypes.byref(p), P(FAKE), 0, P(FAKE), None, None) == -1
+    assert lib.solattn_select_topk(ctypes.byref(p), P(FAKE), 3, None, None, None) == -1
+    assert lib.solattn_select_topk(ctypes.byref(p), P(FAKE), 3, P(FAKE), P(FAKE + 8), None) == -1
+    # top-p: p outside (0, 1], NaN
+    for bad in (0.0, -0.5, 1.5, math.nan):
+        assert lib.solattn_select_topp(ctypes.byref(p), P(FAKE), bad, P(FAKE), None, None) == -1
+    # rows longer than the on-chip sort holds
+    big = sa.problem(1, 1, 128 * 8193, 128, 128, 32, 1.0)
+    assert lib.solattn_select_topk(ctypes.byref(big), P(FAKE), 3, P(FAKE), None, None) == -2
+    assert lib.solattn_select_topp(ctypes.byref(big), P(FAKE), 0.5, P(FAKE), None, None) == -2
+    # unsupported head dim, and empty problems (nothing launched)
+    bad_d = sa.problem(1, 1, 4096, 96, 128, 32, 1.0)
+    assert lib.solattn_proxy_map(ctypes.byref(bad_d), P(FAKE), P(FAKE), P(FAKE), None) == -2
+    empty = sa.problem(0, 4, 4096, 128, 128, 32, 1.0)
+    assert lib.solattn_proxy_map(ctypes.byref(empty), None, None, None, None) == 0
+    assert lib.solattn_select_topk(ctypes.byref(empty), None, 5, None, None, None) == 0
+    assert lib.solattn_select_topp(ctypes.byref(empty), None, 0.5, None, None, None) == 0
