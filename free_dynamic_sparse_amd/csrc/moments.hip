@@ -8,10 +8,11 @@
 // and variance scale^2 * Qbar_i^T Sigma Qbar_i, so all thresholds cost
 // O(N d^2) without the N x N proxy map.
 //
-// Three small kernels, each with a fixed reduction order (deterministic):
-//   kmean_kernel   m = (1/N) sum_j Kbar_j           one workgroup per head
-//   kcov_kernel    Sigma, one 32x32 tile per workgroup, float64 sums of
-//                  centred products staged through LDS
+// Two small kernels, each with a fixed reduction order (deterministic):
+//   kcov_kernel    m = (1/N) sum_j Kbar_j and Sigma, one 32x32 tile of Sigma
+//                  per workgroup (which first forms the means of its 64
+//                  dimensions), float64 sums of centred products staged
+//                  through LDS
 //   tau_kernel     mu_i, sigma_i, tau_i; each thread keeps half a row of
 //                  Sigma in registers and the workgroup walks 32 query blocks
 
@@ -23,39 +24,54 @@
 namespace solattn {
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(256) void kmean_kernel(const float* __restrict__ kbar,
-                                                    float* __restrict__ kmean, uint32_t N) {
-  constexpr int P = 256 / D;  // row phases
-  const int c = threadIdx.x % D;
-  const int p = threadIdx.x / D;
-  const float* src = kbar + (size_t)blockIdx.x * N * D;
-  double s = 0.0;
-  for (uint32_t j = p; j < N; j += P) s += (double)src[(size_t)j * D + c];
-  __shared__ double red[P][D];
-  red[p][c] = s;
-  __syncthreads();
-  if (threadIdx.x < D) {
-    double t = 0.0;
-#pragma unroll
-    for (int q = 0; q < P; ++q) t += red[q][c];
-    kmean[(size_t)blockIdx.x * D + c] = (float)(t / (double)N);
-  }
-}
-
+// Sigma, one 32x32 tile per workgroup, and m.  The workgroup first forms the
+// means of its 32 row-dimensions and 32 column-dimensions (float64 sums over
+// the head's pooled keys in 8 fixed row phases, combined in a fixed order,
+// rounded to float32), then the centred products of those dimensions in
+// float64, staging 64 pooled keys at a time through LDS.  The diagonal tiles
+// also write m.  The head's pooled keys stay in L2 between the two passes.
 template <int D>
 __global__ __launch_bounds__(256) void kcov_kernel(const float* __restrict__ kbar,
-                                                   const float* __restrict__ kmean,
+                                                   float* __restrict__ kmean,
                                                    float* __restrict__ kcov, uint32_t N) {
   constexpr int T = D / 32;  // tiles per dimension
   constexpr int RB = 64;     // pooled keys staged per step
+  constexpr int PH = 256 / 32;  // row phases of the mean pass
   const uint32_t bh = blockIdx.x;
   const int r0 = 32 * (blockIdx.y / T);
   const int c0 = 32 * (blockIdx.y % T);
   const float* src = kbar + (size_t)bh * N * D;
-  const float* m = kmean + (size_t)bh * D;
   __shared__ float sr[RB][33];
   __shared__ float sc[RB][33];
+  __shared__ double part[2][PH][32];
+  __shared__ float mr[32], mc[32];
+
+  {
+    const int ph = threadIdx.x / 32, col = threadIdx.x % 32;
+    double s_r = 0.0, s_c = 0.0;
+    for (uint32_t j = ph; j < N; j += PH) {
+      s_r += (double)src[(size_t)j * D + r0 + col];
+      s_c += (double)src[(size_t)j * D + c0 + col];
+    }
+    part[0][ph][col] = s_r;
+    part[1][ph][col] = s_c;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int which = threadIdx.x / 32;
+      double t = 0.0;
+#pragma unroll
+      for (int q = 0; q < PH; ++q) t += part[which][q][col];
+      const float m = (float)(t / (double)N);
+      if (which == 0) {
+        mr[col] = m;
+        if (r0 == c0) kmean[(size_t)bh * D + r0 + col] = m;
+      } else {
+        mc[col] = m;
+      }
+    }
+    __syncthreads();
+  }
+
   const int ta = threadIdx.x / 16, tb = threadIdx.x % 16;
   double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
   for (uint32_t j0 = 0; j0 < N; j0 += RB) {
@@ -64,8 +80,8 @@ __global__ __launch_bounds__(256) void kcov_kernel(const float* __restrict__ kba
       const uint32_t j = j0 + jj;
       float vr = 0.f, vc = 0.f;
       if (j < N) {
-        vr = src[(size_t)j * D + r0 + col] - m[r0 + col];
-        vc = src[(size_t)j * D + c0 + col] - m[c0 + col];
+        vr = src[(size_t)j * D + r0 + col] - mr[col];
+        vc = src[(size_t)j * D + c0 + col] - mc[col];
       }
       sr[jj][col] = vr;
       sc[jj][col] = vc;
@@ -176,12 +192,9 @@ template <int D>
 hipError_t launch_moments_t(const Shape& s, const float* qbar, const float* kbar, float* kmean,
                             float* kcov, float* tau, float* mu, float* sigma, hipStream_t stream) {
   const uint32_t bh = (uint32_t)s.bh, N = (uint32_t)s.N;
-  hipLaunchKernelGGL((kmean_kernel<D>), dim3(bh), dim3(256), 0, stream, kbar, kmean, N);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((kcov_kernel<D>), dim3(bh, (D / 32) * (D / 32)), dim3(256), 0, stream, kbar,
                      kmean, kcov, N);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((tau_kernel<D>), dim3(bh, (N + 31) / 32), dim3(2 * D), 0, stream, qbar,
                      kmean, kcov, tau, mu, sigma, N, s.scale, s.beta);
