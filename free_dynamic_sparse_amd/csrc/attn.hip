@@ -17,23 +17,18 @@
 //
 // The nested loop of Algorithm 3.2, reordered for latency (the selected set
 // is the union of the chunks' sets, so the order changes nothing):
-//   * routing: every pooled key is tested against both thresholds up front
-//     (shat_ij = scale * Qbar_i . Kbar_j in float32, one key per thread; the
-//     page reads these scores off the token-to-block tile as column means,
-//     the same number, which a bf16 tile could not resolve inside the tie
-//     band); the selected bits stay in an on-chip bitmap;
-//   * approximation: the pooled keys are staged 32 at a time into LDS as
-//     bf16 tiles (Kbar in the K layout, Vhat in the V layout; the next 32 in
-//     registers meanwhile); the token-to-block tile scale * Q_i KC^T (MFMA)
-//     gives the logits of the unselected columns, which enter the group's
-//     online softmax with weight n_j and value Vhat_j;
-//   * exact attention: the selected blocks of both groups run back to back
-//     in increasing order with the next block's K/V always in flight: K and
-//     V are double-buffered in LDS, loaded with direct-to-LDS loads
-//     (global_load_lds_dwordx4, 1 KB per wave instruction) into XOR-swizzled
-//     tiles, one workgroup barrier per key block.  Each block is processed
-//     in 32-key tiles so that a tile's exponentials overlap the next tile's
-//     score MFMAs.
+//   * routing and approximation, one pass over the pooled keys, 64 at a
+//     time: the float32 rows of Kbar and Vhat are loaded once (whole
+//     128-byte lines per instruction, the next 64 rows in flight meanwhile);
+//     the routing scores shat_ij = scale * Qbar_i . Kbar_j are formed from
+//     them in float32 for both query blocks and tested against the
+//     thresholds, and the decisions go to on-chip bitmaps (the page reads
+//     these scores off the token-to-block tile as column means: the same
+//     numbers, which a bf16 tile could not resolve inside the tie band); the
+//     same registers are stored to LDS as bf16 tiles (Kbar in the K layout,
+//     Vhat in the V layout), and the token-to-block tile scale * Q_i KC^T
+//     (MFMA) gives the logits of the unselected columns, which enter the
+//     group's online softmax with weight n_j and value Vhat_j;
 // Exact and approximate terms share one running max, denominator and
 // accumulator; the order in which they enter is immaterial to the result.
 //
