@@ -236,6 +236,21 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0
     return out
 
 
+def stats(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0,
+          block: int = 128, chunk: int = 32, scale: Optional[float] = None,
+          exact_only: bool = False, stream=None) -> dict:
+    """The forward with every routing statistic returned: a dict of the
+    output `out` and the thresholds `tau`, row means `mu` and standard
+    deviations `sigma` [B, H, N], the selection bitmaps `sel_mask`
+    [B, H, N, ceil(N/64)] (int64 words) and counts `sel_count` [B, H, N]."""
+    B, H, L, d = q.shape
+    p = problem(B, H, L, d, block, chunk, beta, scale, exact_only)
+    ws = Workspace(p, q.device, debug=True)
+    out = forward(q, k, v, beta, block, chunk, scale, exact_only, ws=ws, stream=stream)
+    return dict(out=out, tau=ws.tau, mu=ws.mu, sigma=ws.sigma, sel_mask=ws.sel_mask,
+                sel_count=ws.sel_count)
+
+
 def dense_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int = 128,
                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:

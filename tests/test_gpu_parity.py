@@ -293,3 +293,22 @@ def test_seq_sweep_shapes(sa, L, beta):
     # the sequence-length sweep's shortest and longest shapes, in the
     # configuration the sweep times
     full_size(sa, synth.seq_workload(L), beta, heads_checked=(0, 7), n_rows=3)
+
+
+def test_stats_returns_the_routing_statistics(sa):
+    # the Python convenience entry: the same statistics as the oracle
+    w = synth.WORKLOADS["image"].replace(H=3)
+    q, k, v = synth.make_inputs(w)
+    res = sa.stats(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), beta=1.0, block=w.block,
+                   chunk=w.chunk)
+    torch.cuda.synchronize()
+    N = w.N
+    sel = sa.mask_to_bool(res["sel_mask"], N).numpy()
+    for h in range(w.H):
+        r = ref.solattn_head(q[0, h], k[0, h], v[0, h], 1.0, w.block, rows=[])
+        g = {"tau": res["tau"][0, h].cpu().numpy(), "mu": res["mu"][0, h].cpu().numpy(),
+             "sigma": res["sigma"][0, h].cpu().numpy()}
+        parity.check_stats(g, r, 1.0)
+        st = parity.selection_check(sel[0, h], r)
+        assert st.hard == 0
+        np.testing.assert_array_equal(res["sel_count"][0, h].cpu().numpy(), sel[0, h].sum(axis=1))
