@@ -7,10 +7,11 @@
 //
 // One workgroup per (b, h, block): 256 threads read the block's Q, K and V
 // rows as coalesced 16-byte loads (each thread owns one 8-column segment of
-// a row and walks rows with a fixed stride), accumulate in float32
-// registers, and reduce the row phases through LDS in a fixed order.  The
-// pass is bound by HBM reads: 3 * n_j * d * 2 bytes per block, streamed with
-// non-temporal loads (7 % faster at the Wan shape than cached loads).
+// a row and walks rows with a fixed stride), issue all of them before the
+// first add, accumulate in float32 registers, and reduce the row phases
+// through LDS in a fixed order.  The pass is bound by HBM reads:
+// 3 * n_j * d * 2 bytes per block, streamed with non-temporal loads (7 %
+// faster at the Wan shape than cached loads).
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -46,23 +47,25 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
     for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
 
   const uint16_t* src[3] = {q + base, k + base, v + base};
+  u32x4 w[STEPS][3];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int row = r + s * RPS;
-    if (row < n) {
 #pragma unroll
-      for (int t = 0; t < 3; ++t) {
-        // read once and never again by this kernel: keep it out of the caches
-        const u32x4 w =
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src[t] + (size_t)row * D));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[t][2 * e] += bf16_bits_to_f32(w[e] & 0xffffu);
-          acc[t][2 * e + 1] += bf16_bits_to_f32(w[e] >> 16);
-        }
-      }
-    }
+    for (int t = 0; t < 3; ++t)
+      w[s][t] = row < n ? __builtin_nontemporal_load(
+                              reinterpret_cast<const u32x4*>(src[t] + (size_t)row * D))
+                        : u32x4{0u, 0u, 0u, 0u};
   }
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[t][2 * e] += bf16_bits_to_f32(w[s][t][e] & 0xffffu);
+        acc[t][2 * e + 1] += bf16_bits_to_f32(w[s][t][e] >> 16);
+      }
 
   __shared__ float red[RPS][3 * D];
 #pragma unroll
