@@ -106,16 +106,11 @@ __global__ __launch_bounds__(256) void kcov_kernel(const float* __restrict__ kba
       dst[(size_t)(r0 + 2 * ta + x) * D + c0 + 2 * tb + y] = (float)(acc[x][y] / (double)N);
 }
 
-// Sum over the workgroup of one value per thread; fixed order.
-template <int NT>
-__device__ __forceinline__ float block_sum_to(float x, float* slot, int g) {
-  // wave-level butterfly, then lane 0 writes the wave total
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  if ((threadIdx.x % kWave) == 0) slot[(threadIdx.x / kWave) * 64 + g] = x;
-  return x;
-}
-
+// mu_i, sigma_i and tau_i for 32 query blocks per workgroup.  Each thread
+// keeps half a row r of Sigma in registers and forms (Sigma Qbar_i)_r for the
+// 32 blocks; the per-dimension terms Qbar_ir (Sigma Qbar_i)_r and Qbar_ir m_r
+// go to LDS, and TPG threads per block then sum them over r in a fixed order
+// (a run of D / TPG dimensions each, then lane exchanges).
 template <int D>
 __global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kmean,
@@ -123,7 +118,10 @@ __global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qb
                                                     float* __restrict__ tau, float* __restrict__ mu,
                                                     float* __restrict__ sigma, uint32_t N,
                                                     float scale, float beta) {
-  constexpr int NT = 2 * D, HALF = D / 2, G = 32, NW = NT / kWave;
+  constexpr int NT = 2 * D, HALF = D / 2, G = 32;
+  constexpr int TPG = NT / G;      // threads per query block in the final sums
+  constexpr int RUN = D / TPG;     // dimensions summed by each of them
+  static_assert(TPG * RUN == D && (TPG & (TPG - 1)) == 0, "reduction shape");
   const uint32_t bh = blockIdx.x;
   const uint32_t i0 = blockIdx.y * G;
   const int t = threadIdx.x, r = t / 2, h = t % 2;
@@ -136,8 +134,8 @@ __global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qb
 
   __shared__ float qs[G][D];
   __shared__ float ms[D];
-  __shared__ float red_q[NW * 64];
-  __shared__ float red_m[NW * 64];
+  __shared__ float pq[G][D + 1];  // Qbar_ir (Sigma Qbar_i)_r
+  __shared__ float pm[G][D + 1];  // Qbar_ir m_r
   for (int e = t; e < G * D; e += NT) {
     const int g = e / D, c = e % D;
     const uint32_t i = i0 + g;
@@ -152,39 +150,42 @@ __global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qb
 #pragma unroll
     for (int e = 0; e < HALF; ++e) y = fmaf(srow[e], qv[h * HALF + e], y);
     const float other = __shfl_xor(y, 1);
-    const float yr = (h == 0) ? (y + other) : (other + y);  // (Sigma Qbar)_r
-    const float cq = (h == 0) ? yr * qv[r] : 0.f;            // Qbar_r (Sigma Qbar)_r
-    const float cm = (h == 0) ? ms[r] * qv[r] : 0.f;         // Qbar_r m_r
-    block_sum_to<NT>(cq, red_q, g);
-    block_sum_to<NT>(cm, red_m, g);
+    if (h == 0) {
+      pq[g][r] = (y + other) * qv[r];  // (Sigma Qbar)_r, the two halves in a fixed order
+      pm[g][r] = ms[r] * qv[r];
+    }
   }
   __syncthreads();
 
-  if (t < G) {
-    const uint32_t i = i0 + t;
-    if (i < N) {
-      float qf = 0.f, md = 0.f;
+  const int g = t / TPG, part = t % TPG;
+  float qf = 0.f, md = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        qf += red_q[w * 64 + t];
-        md += red_m[w * 64 + t];
-      }
-      const float mu_i = scale * md;
-      const float sigma_i = sqrtf(fmaxf(scale * scale * qf, 0.f));
-      float tau_i;
-      if (beta == -INFINITY)
-        tau_i = -INFINITY;
-      else if (beta == INFINITY)
-        tau_i = INFINITY;
-      else if (sigma_i == 0.f)
-        tau_i = -INFINITY;  // constant proxy row: every block passes the >= test
-      else
-        tau_i = mu_i + beta * sigma_i;
-      const size_t o = (size_t)bh * N + i;
-      tau[o] = tau_i;
-      if (mu) mu[o] = mu_i;
-      if (sigma) sigma[o] = sigma_i;
-    }
+  for (int e = 0; e < RUN; ++e) {
+    qf += pq[g][part * RUN + e];
+    md += pm[g][part * RUN + e];
+  }
+#pragma unroll
+  for (int o = TPG / 2; o >= 1; o /= 2) {
+    qf += __shfl_xor(qf, o);
+    md += __shfl_xor(md, o);
+  }
+  const uint32_t i = i0 + g;
+  if (part == 0 && i < N) {
+    const float mu_i = scale * md;
+    const float sigma_i = sqrtf(fmaxf(scale * scale * qf, 0.f));
+    float tau_i;
+    if (beta == -INFINITY)
+      tau_i = -INFINITY;
+    else if (beta == INFINITY)
+      tau_i = INFINITY;
+    else if (sigma_i == 0.f)
+      tau_i = -INFINITY;  // constant proxy row: every block passes the >= test
+    else
+      tau_i = mu_i + beta * sigma_i;
+    const size_t o = (size_t)bh * N + i;
+    tau[o] = tau_i;
+    if (mu) mu[o] = mu_i;
+    if (sigma) sigma[o] = sigma_i;
   }
 }
 
