@@ -65,7 +65,6 @@ struct Cfg {
   static constexpr int KS = D / 16;         // k-steps of Q K^T (contraction over d)
   static constexpr int MT = BLK / 32;       // 32-key tiles of S^T
   static constexpr int DT = D / 32;         // 32-wide d tiles of O^T
-  static constexpr int PK = BLK / 16;       // k-steps of P V (contraction over keys)
   static constexpr int SEGS = D / 8;        // 16-byte segments in a bf16 row
   static constexpr int ROW = 2 * D;         // bytes per bf16 row
   static constexpr int TILE = BLK * ROW;    // bytes per K or V tile
@@ -107,7 +106,6 @@ struct AttnArgs {
   uint32_t N;
   uint32_t pairs;    // ceil(N / 2)
   uint32_t per_xcd;  // pairs per XCD slab: ceil(pairs / 8)
-  int chunk;
   float scale;
   float c_log2;      // scale * log2(e): logits enter exp2 in this unit
   uint32_t exact_only;
@@ -834,7 +832,6 @@ hipError_t launch_attn(const Shape& s, AttnArgs a, hipStream_t stream) {
   a.N = (uint32_t)s.N;
   a.pairs = (uint32_t)((s.N + 1) / 2);
   a.per_xcd = (a.pairs + kXcds - 1) / kXcds;
-  a.chunk = s.chunk;
   a.scale = s.scale;
   a.c_log2 = s.scale * kLog2e;
   const dim3 grid((uint32_t)(kXcds * a.per_xcd * s.bh));

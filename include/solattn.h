@@ -55,7 +55,9 @@ extern "C" {
  *                         block x block tiles for queries and keys alike).
  *  chunk                  C, pooled keys per routing chunk, 1..64.  C changes
  *                         the schedule, never the result (method section,
- *                         chunk-wise streaming thresholding).
+ *                         chunk-wise streaming thresholding); it is validated
+ *                         and the fused kernel routes 64 pooled keys per step
+ *                         whatever its value.
  *  beta                   standardized cutoff of tau_i = mu_i + beta*sigma_i
  *                         (Eq. 4).  Any finite value; -INFINITY selects every
  *                         block, +INFINITY none.  NaN is rejected.
