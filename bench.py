@@ -302,6 +302,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan")
+    ap.add_argument("--block", type=int, default=0,
+                    help="tokens per block (64 or 128); default: the workload's own (128)")
     ap.add_argument("--beta", type=float, default=1.0)
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
@@ -350,6 +352,8 @@ def main() -> int:
         return 0
 
     w = synth.WORKLOADS[args.workload]
+    if args.block:
+        w = w.replace(block=args.block)
     t0 = time.time()
     qb, kb, vb = synth.make_inputs_bf16_bits(w)
     dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
@@ -446,11 +450,13 @@ def main() -> int:
         "fwd_executed_tflops": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12,
         "dense_equivalent_tflops": dense_equiv / (t["total_ms"] * 1e-3) / 1e12,
         "pool_hbm_gbps": pool_bytes / (t["pool_ms"] * 1e-3) / 1e9,
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel<128,128,fused> (solattn_fwd)",
+        "roofline": {"bound": "mfma", "kernel": f"attn_kernel<{d},{w.block},fused> (solattn_fwd)",
                      "achieved": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic()},
+                     # counters were taken on the default workload only
+                     "traffic": measured_traffic() if (w.name, w.block, beta) == ("wan", 128, 1.0)
+                     else None},
     }
 
     if not args.skip_dense:

@@ -312,3 +312,11 @@ def test_stats_returns_the_routing_statistics(sa):
         st = parity.selection_check(sel[0, h], r)
         assert st.hard == 0
         np.testing.assert_array_equal(res["sel_count"][0, h].cpu().numpy(), sel[0, h].sum(axis=1))
+
+
+@pytest.mark.timeout(300)
+def test_wan_full_size_block64(sa):
+    # the page's 64-token blocks at the Wan shape (N = 1182, tail 16): every
+    # head's selection and statistics, sampled heads' outputs
+    full_size(sa, synth.WORKLOADS["wan"].replace(block=64, H=16), 1.0, heads_checked=(0, 15),
+              n_rows=4)
