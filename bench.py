@@ -231,7 +231,11 @@ def routing_study(sa, w: synth.Workload, beta: float):
     tested on chip, a pass measured alone (exact-only at beta = +inf: it also
     reads Q and writes O) as an upper bound.  Top-k / top-p: the proxy map
     plus the per-row selection; k = the threshold router's mean count, p found
-    by bisection to give the same mean density."""
+    by bisection to give the same mean density.
+
+    Accuracy at that density: each rule's selections drive the same fused
+    kernel (solattn_fwd_masked for top-k and top-p), with and without the
+    approximation of the other blocks; errors are against the dense kernel."""
     q, k, v = _to_device(w)
     B, H, L, d = q.shape
     N = w.N
@@ -251,8 +255,24 @@ def routing_study(sa, w: synth.Workload, beta: float):
     sa.solattn_moments(p_inf, ws.qbar, ws.kbar, ws_inf.kmean, ws_inf.kcov, ws_inf.tau)
     t_pass = _time_ms(lambda: sa.solattn_fwd(p_inf, q, k, v, ws.qbar, ws.kbar, ws.vhat,
                                              ws_inf.tau, out), 5)
-    del q, k, v, out
-    torch.cuda.empty_cache()
+    dense = torch.empty_like(q)
+    sa.solattn_dense_fwd(sa.problem(B, H, L, d, w.block, w.chunk, -math.inf), q, k, v, dense)
+    p_eo = sa.problem(B, H, L, d, w.block, w.chunk, beta, None, True)
+
+    def accuracy(sel_mask):
+        """rel-l2 / cosine against dense, full and exact-only, for given selections."""
+        res = {}
+        for mode, pp in (("full", p), ("exact_only", p_eo)):
+            if sel_mask is None:
+                sa.solattn_fwd(pp, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out)
+            else:
+                sa.solattn_fwd_masked(pp, q, k, v, ws.kbar, ws.vhat, sel_mask, out)
+            torch.cuda.synchronize()
+            rel, cos = _errors(out, dense)
+            res[mode] = {"rel_l2_mean": float(rel.mean()), "cosine_mean": float(cos.mean())}
+        return res
+
+    acc_thr = accuracy(None)
 
     shat = torch.empty((B, H, N, N), dtype=torch.float32, device="cuda")
     mask = torch.empty((B, H, N, (N + 63) // 64), dtype=torch.int64, device="cuda")
@@ -261,6 +281,7 @@ def routing_study(sa, w: synth.Workload, beta: float):
     kk = max(1, int(round(rho * N)))
     t_topk = _time_ms(lambda: sa.solattn_select_topk(p, shat, kk, mask, cnt), 10)
     dens_topk = cnt.double().cpu().numpy() / N
+    acc_topk = accuracy(mask)
 
     def topp_density(pp):
         sa.solattn_select_topp(p, shat, pp, mask, cnt)
@@ -276,6 +297,9 @@ def routing_study(sa, w: synth.Workload, beta: float):
     top_p = hi
     t_topp = _time_ms(lambda: sa.solattn_select_topp(p, shat, top_p, mask, cnt), 10)
     dens_topp = cnt.double().cpu().numpy() / N
+    acc_topp = accuracy(mask)
+    del q, k, v, out, dense
+    torch.cuda.empty_cache()
 
     f32 = 4
     mem_thr = B * H * (d + d * d + N) * f32  # m, Sigma, tau
@@ -283,12 +307,13 @@ def routing_study(sa, w: synth.Workload, beta: float):
     ours = t_moments
     rows = {
         "threshold": {"beta": beta, "routing_ms": ours, "in_kernel_pass_ms_upper": t_pass,
-                      "memory_bytes": mem_thr, "density": _spread(dens_thr)},
+                      "memory_bytes": mem_thr, "density": _spread(dens_thr),
+                      "accuracy": acc_thr},
         "top_k": {"k": kk, "routing_ms": t_map + t_topk, "map_ms": t_map, "select_ms": t_topk,
-                  "memory_bytes": mem_map, "density": _spread(dens_topk),
+                  "memory_bytes": mem_map, "density": _spread(dens_topk), "accuracy": acc_topk,
                   "slowdown_vs_threshold": (t_map + t_topk) / ours},
         "top_p": {"p": top_p, "routing_ms": t_map + t_topp, "map_ms": t_map, "select_ms": t_topp,
-                  "memory_bytes": mem_map, "density": _spread(dens_topp),
+                  "memory_bytes": mem_map, "density": _spread(dens_topp), "accuracy": acc_topp,
                   "slowdown_vs_threshold": (t_map + t_topp) / ours},
     }
     log(f"routing {rows}")

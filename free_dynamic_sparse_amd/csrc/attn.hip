@@ -102,6 +102,7 @@ struct AttnArgs {
   uint16_t* out;
   uint64_t* sel_mask;
   int32_t* sel_count;
+  const uint64_t* sel_in;  // given selections (masked mode) or null (threshold routing)
   int64_t L;
   uint32_t N;
   uint32_t pairs;    // ceil(N / 2)
@@ -670,13 +671,14 @@ __device__ __forceinline__ void approx_sub(const char* kt, const char* vt,
 // is used; staging buffers alternate between the two K / V tile buffers,
 // which are free until the exact phase starts, so each sub-chunk costs one
 // workgroup barrier.  On return both groups' bitmaps are complete and the
-// tile buffers are free.
+// tile buffers are free.  With route false the bitmaps are given (filled
+// before the call) and only the approximation runs.
 template <int D, int BLK>
 __device__ __forceinline__ void route_approx_phase(
     char* smem, uint32_t (*bits)[kMaxBlocks / 32], const float (*qbar_s)[D], const float* kbar_h,
     const float* vhat_h, uint32_t N, int n_last, float tau0, float tau1, float scale,
-    bool approx, bool grp_on, int grp, const bf16x8* qreg, float c, float& m_run, float& l_run,
-    f32x16* o, int tid, int wave, int lane) {
+    bool route, bool approx, bool grp_on, int grp, const bf16x8* qreg, float c, float& m_run,
+    float& l_run, f32x16* o, int tid, int wave, int lane) {
   using C = Cfg<D, BLK>;
   static_assert(C::SUB == 64 && C::SUB <= BLK, "a staged sub-chunk is one 64-bit word per group");
   using Stage = PooledStage<D, BLK>;
@@ -691,7 +693,7 @@ __device__ __forceinline__ void route_approx_phase(
   for (uint32_t sb = 0; sb < nsub; ++sb) {
     char* kt = smem + (buf ? C::K1 : C::K0);
     char* vt = smem + (buf ? C::V1 : C::V0);
-    st.route(bits0, bits1, qbar_s, tau0, tau1, scale, sb * C::SUB, N, tid, lane, wave);
+    if (route) st.route(bits0, bits1, qbar_s, tau0, tau1, scale, sb * C::SUB, N, tid, lane, wave);
     st.store(kt, vt, tid);
     if (sb + 1 < nsub) st.load(kbar_h, vhat_h, (sb + 1) * C::SUB, N, tid);
     __syncthreads();  // staged rows and their bits visible; the other buffer's readers are done
@@ -762,19 +764,35 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   if constexpr (FUSED) {
     // ---- outer loop: routing and approximation, sub-chunk by sub-chunk
     const uint32_t item0 = bh * N + 2 * pair;
-    const float tau0 = a.tau[item0];
-    const float tau1 = pair1_on ? a.tau[item0 + 1] : INFINITY;
-    for (int cc = tid; cc < 2 * D; cc += C::NT) {
-      const int gq = cc / D;
-      qbar_s[gq][cc % D] =
-          (gq == 0 || pair1_on) ? a.qbar[(size_t)(item0 + gq) * D + cc % D] : 0.f;
+    const bool route = a.sel_in == nullptr;
+    float tau0 = INFINITY, tau1 = INFINITY;
+    if (route) {
+      tau0 = a.tau[item0];
+      tau1 = pair1_on ? a.tau[item0 + 1] : INFINITY;
+      for (int cc = tid; cc < 2 * D; cc += C::NT) {
+        const int gq = cc / D;
+        qbar_s[gq][cc % D] =
+            (gq == 0 || pair1_on) ? a.qbar[(size_t)(item0 + gq) * D + cc % D] : 0.f;
+      }
+    } else {
+      // masked mode: the two query blocks' given rows, with any bit at or
+      // past N cleared so that the walk never visits a block that does not exist
+      const uint32_t W64 = (N + 63) / 64;
+      for (uint32_t e = tid; e < 2 * W64; e += C::NT) {
+        const uint32_t gq = e / W64, w = e % W64;
+        uint64_t word = (gq == 0 || pair1_on) ? a.sel_in[(size_t)(item0 + gq) * W64 + w] : 0ull;
+        const uint32_t rows = N - 64 * w;
+        if (rows < 64u) word &= (1ull << rows) - 1ull;
+        selbits[gq][2 * w] = (uint32_t)word;
+        selbits[gq][2 * w + 1] = (uint32_t)(word >> 32);
+      }
     }
     const uint32_t words = (N + 31) / 32;
     const float* kbar_h = a.kbar + (size_t)bh * N * D;
     const float* vhat_h = a.vhat + (size_t)bh * N * D;
     __syncthreads();
     route_approx_phase<D, BLK>(smem, selbits, qbar_s, kbar_h, vhat_h, N,
-                               (int)(L - (int64_t)(N - 1) * BLK), tau0, tau1, a.scale,
+                               (int)(L - (int64_t)(N - 1) * BLK), tau0, tau1, a.scale, route,
                                !a.exact_only, grp_on, grp, qreg, a.c_log2, m_run, l_run, o, tid,
                                wave, lane);
 
@@ -855,7 +873,8 @@ int64_t fused_max_blocks() { return kMaxBlocks; }
 
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,
-                      void* out, uint64_t* sel_mask, int32_t* sel_count, hipStream_t stream) {
+                      const uint64_t* sel_in, void* out, uint64_t* sel_mask, int32_t* sel_count,
+                      hipStream_t stream) {
   AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -867,6 +886,7 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
   a.out = static_cast<uint16_t*>(out);
   a.sel_mask = sel_mask;
   a.sel_count = sel_count;
+  a.sel_in = sel_in;
   a.exact_only = (s.flags & 1u) ? 1u : 0u;
   return launch_attn<true>(s, a, stream);
 }

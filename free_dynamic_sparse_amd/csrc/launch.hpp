@@ -28,9 +28,12 @@ hipError_t launch_moments(const Shape& s, const float* qbar, const float* kbar, 
 // Largest N = ceil(L / block) the fused kernel keeps on-chip selection bits for.
 int64_t fused_max_blocks();
 
+// sel_in null: threshold routing from qbar and tau.  Otherwise the given
+// selections (qbar and tau unused).
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,
-                      void* out, uint64_t* sel_mask, int32_t* sel_count, hipStream_t stream);
+                      const uint64_t* sel_in, void* out, uint64_t* sel_mask, int32_t* sel_count,
+                      hipStream_t stream);
 
 hipError_t launch_dense(const Shape& s, const void* q, const void* k, const void* v, void* out,
                         hipStream_t stream);

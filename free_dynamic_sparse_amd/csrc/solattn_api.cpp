@@ -100,8 +100,24 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
       !ok_ptr(vhat) || !ok_ptr(tau) || !ok_ptr(out) || !ok_opt_ptr(sel_mask) ||
       !ok_opt_ptr(sel_count))
     return SOLATTN_E_INVALID_ARG;
-  return from_hip(solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, out, sel_mask,
+  return from_hip(solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, nullptr, out, sel_mask,
                                       sel_count, static_cast<hipStream_t>(stream)));
+}
+
+int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                       const float* kbar, const float* vhat, const uint64_t* sel_in, void* out,
+                       void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (s.N > solattn::fused_max_blocks()) return SOLATTN_E_UNSUPPORTED;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(kbar) || !ok_ptr(vhat) ||
+      !ok_ptr(sel_in) || !ok_ptr(out))
+    return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_fwd(s, q, k, v, nullptr, kbar, vhat, nullptr, sel_in, out,
+                                      nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int solattn_dense_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,

@@ -24,7 +24,8 @@ SOLATTN_E_UNSUPPORTED = -2
 SOLATTN_E_HIP = -3
 SOLATTN_FLAG_EXACT_ONLY = 1
 
-EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd",
+EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_masked",
+           "solattn_dense_fwd",
            "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp",
            "solattn_strerror", "solattn_version")
 
@@ -56,11 +57,12 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.solattn_moments.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_dense_fwd.argtypes = [pp, vp, vp, vp, vp, vp]
+    lib.solattn_fwd_masked.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_proxy_map.argtypes = [pp, vp, vp, vp, vp]
     lib.solattn_select_topk.argtypes = [pp, vp, ctypes.c_int64, vp, vp, vp]
     lib.solattn_select_topp.argtypes = [pp, vp, ctypes.c_float, vp, vp, vp]
-    for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_dense_fwd",
-                 "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp"):
+    for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_masked",
+                 "solattn_dense_fwd", "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp"):
         getattr(lib, name).restype = ctypes.c_int
     lib.solattn_strerror.argtypes = [ctypes.c_int]
     lib.solattn_strerror.restype = ctypes.c_char_p
@@ -160,6 +162,18 @@ def solattn_fwd(p: Problem, q, k, v, qbar, kbar, vhat, tau, out, sel_mask=None, 
                            _stream(stream)), "solattn_fwd")
 
 
+def solattn_fwd_masked(p: Problem, q, k, v, kbar, vhat, sel_in, out, stream=None) -> None:
+    full, pooled, N = _dims(p)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, full, n)
+    for t, n in ((kbar, "kbar"), (vhat, "vhat")):
+        _need(t, torch.float32, pooled, n)
+    _need(sel_in, torch.int64, (p.batch, p.heads, N, (N + 63) // 64), "sel_in")
+    _check(LIB.solattn_fwd_masked(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar),
+                                  _ptr(vhat), _ptr(sel_in), _ptr(out), _stream(stream)),
+           "solattn_fwd_masked")
+
+
 def solattn_dense_fwd(p: Problem, q, k, v, out, stream=None) -> None:
     full, _, _ = _dims(p)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
@@ -249,6 +263,33 @@ def stats(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0,
     out = forward(q, k, v, beta, block, chunk, scale, exact_only, ws=ws, stream=stream)
     return dict(out=out, tau=ws.tau, mu=ws.mu, sigma=ws.sigma, sel_mask=ws.sel_mask,
                 sel_count=ws.sel_count)
+
+
+def forward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_mask: torch.Tensor,
+                   block: int = 128, scale: Optional[float] = None, exact_only: bool = False,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The forward with given selections (int64 bitmaps [B, H, N, ceil(N/64)]):
+    pool, then the fused kernel without routing."""
+    B, H, L, d = q.shape
+    p = problem(B, H, L, d, block, 32, 1.0, scale, exact_only)
+    ws = Workspace(p, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, stream)
+    solattn_fwd_masked(p, q, k, v, ws.kbar, ws.vhat, sel_mask, out, stream)
+    return out
+
+
+def bool_to_mask(sel: torch.Tensor) -> torch.Tensor:
+    """Pack bool [..., N] into the u64 row bitmaps [..., ceil(N/64)] (CPU,
+    as int64 words)."""
+    sel = sel.cpu().bool()
+    N = sel.shape[-1]
+    W = (N + 63) // 64
+    padded = torch.zeros(*sel.shape[:-1], W * 64, dtype=torch.int64)
+    padded[..., :N] = sel.to(torch.int64)
+    bits = padded.reshape(*sel.shape[:-1], W, 64) << torch.arange(64, dtype=torch.int64)
+    return bits.sum(dim=-1)
 
 
 def dense_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block: int = 128,

@@ -140,6 +140,25 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
                 void* out, uint64_t* sel_mask, int32_t* sel_count, void* stream);
 
 /*
+ * The fused forward with the selected sets given instead of routed: the
+ * same kernel and arithmetic as solattn_fwd (exact attention over the given
+ * blocks, the zeroth-order terms of every other block unless
+ * SOLATTN_FLAG_EXACT_ONLY), for comparing routing rules at identical block
+ * indices (the page's comparisons at identical selections, experiments
+ * section, Figures 7 and 8).
+ *   q, k, v    in:  bf16 [B, H, L, d]
+ *   kbar, vhat in:  f32 [B, H, N, d]  from solattn_pool
+ *   sel_in     in:  u64 [B, H, N, ceil(N/64)], solattn_fwd's sel_mask layout
+ *              (e.g. from solattn_select_topk / solattn_select_topp); bits
+ *              at or past N are ignored
+ *   out        out: bf16 [B, H, L, d]
+ * beta and chunk are ignored.  Same limit as solattn_fwd (N <= 8192).
+ */
+int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                       const float* kbar, const float* vhat, const uint64_t* sel_in, void* out,
+                       void* stream);
+
+/*
  * Dense softmax attention softmax(scale * Q K^T) V on the same MFMA core,
  * block by block with one online softmax (no routing).  beta, chunk and
  * flags are ignored; block picks the tile size.

@@ -161,3 +161,20 @@ def test_baseline_entry_points_reject_bad_arguments(sa):
     assert lib.solattn_proxy_map(ctypes.byref(empty), None, None, None, None) == 0
     assert lib.solattn_select_topk(ctypes.byref(empty), None, 5, None, None, None) == 0
     assert lib.solattn_select_topp(ctypes.byref(empty), None, 0.5, None, None, None) == 0
+
+
+def test_masked_forward_rejects_bad_arguments(sa):
+    p = sa.problem(1, 2, 4096, 128, 128, 32, 1.0)
+    P = lambda x: ctypes.c_void_p(x)
+    lib = sa.LIB
+    # q, k, v, kbar, vhat, sel_in, out: each null or misaligned in turn
+    for i in range(7):
+        args = [P(FAKE)] * 7
+        args[i] = None
+        assert lib.solattn_fwd_masked(ctypes.byref(p), *args, None) == -1
+        args[i] = P(FAKE + 8)
+        assert lib.solattn_fwd_masked(ctypes.byref(p), *args, None) == -1
+    big = sa.problem(1, 1, 128 * 8193, 128, 128, 32, 1.0)
+    assert lib.solattn_fwd_masked(ctypes.byref(big), *([P(FAKE)] * 7), None) == -2
+    empty = sa.problem(2, 0, 4096, 128, 128, 32, 1.0)
+    assert lib.solattn_fwd_masked(ctypes.byref(empty), *([None] * 7), None) == 0

@@ -320,3 +320,50 @@ def test_wan_full_size_block64(sa):
     # head's selection and statistics, sampled heads' outputs
     full_size(sa, synth.WORKLOADS["wan"].replace(block=64, H=16), 1.0, heads_checked=(0, 15),
               n_rows=4)
+
+
+# ------------------------------------------------------------ given selections
+
+@pytest.mark.parametrize("exact_only", [False, True])
+def test_masked_forward_with_topk_selections(sa, exact_only):
+    # the oracle's top-k sets (an upper set of each proxy row of a fixed
+    # size) as the given selections: the fused kernel without routing against
+    # the oracle's forward over the same sets
+    for w, kk in ((synth.WORKLOADS["image"].replace(H=3), 6),
+                  (synth.Workload("ragged_m", B=2, H=2, L=3000, d=128, block=128, chunk=32,
+                                  seed=27, kind="pos", grid=(1, 1, 3000)), 5)):
+        q, k, v = synth.make_inputs(w)
+        sels = np.zeros((w.B, w.H, w.N, w.N), dtype=bool)
+        for b in range(w.B):
+            for h in range(w.H):
+                qb, kb, _ = ref.pool(q[b, h], k[b, h], v[b, h], w.block)
+                sels[b, h] = ref.select_topk(ref.proxy_scores(qb, kb, ref.default_scale(w.d)), kk)
+        mask = sa.bool_to_mask(torch.from_numpy(sels)).cuda()
+        out = sa.forward_masked(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), mask,
+                                block=w.block, exact_only=exact_only)
+        got = out.float().cpu().numpy()
+        for b in range(w.B):
+            for h in range(w.H):
+                want = ref.forward(q[b, h], k[b, h], v[b, h], sels[b, h], w.block,
+                                   ref.default_scale(w.d), exact_only)
+                max_abs, mean_rel, finite = parity.output_errors(got[b, h], want)
+                log(f"  masked {w.name} b{b} h{h} exact_only={exact_only}: max_abs={max_abs:.3g} "
+                    f"mean_rel={mean_rel:.3g}")
+                assert finite and max_abs <= parity.MAX_ABS and mean_rel <= parity.MEAN_REL
+
+
+def test_masked_forward_reproduces_routed_forward(sa):
+    # fed the routed kernel's own selections (with garbage in the bits past
+    # N), the masked kernel does the same work in the same order: equal bits
+    w = synth.Workload("mask_same", B=1, H=4, L=4096 + 200, d=128, block=128, chunk=32, seed=28,
+                       kind="pos", grid=(1, 1, 4096 + 200))
+    q, k, v = (to_dev_bf16(x) for x in synth.make_inputs(w))
+    res = sa.stats(q, k, v, beta=1.0, block=w.block, chunk=w.chunk)
+    mask = res["sel_mask"].clone()
+    N = w.N
+    assert N % 64 != 0
+    junk = torch.tensor(-1 << (N % 64), dtype=torch.int64)  # every bit at or past N
+    mask[..., -1] |= junk.cuda()
+    out = sa.forward_masked(q, k, v, mask, block=w.block)
+    torch.cuda.synchronize()
+    assert torch.equal(out, res["out"])
