@@ -11,7 +11,8 @@ moment-based row statistics (the moment identity of Appendix B), chunk-wise
 streaming thresholding (Eqs. 6-7), the zeroth-order Taylor approximation of
 unselected blocks (the expansion before Eqs. 9-10), the combined denominator
 and numerator (Eqs. 9-10), the token-to-block score tile (Eq. 11, Figure 4)
-and the nested-loop kernel (Algorithm 3.2).
+and the nested-loop kernel (Algorithm 3.2).  Beyond the page's method,
+first_order_terms keeps the first-order term of the same Taylor expansion.
 
 Everything is plain NumPy in float64 on one (batch, head) at a time, written
 for a reader checking it against the page, not for speed.  Where the page
@@ -39,6 +40,14 @@ Pins (tests/test_oracle_*.py, CPU only):
   select_topp          mass reaches p and the prefix is the shortest such
                        (invariants); uniform rows keep ceil(p N) blocks, a
                        dominant score keeps one, p = 1 keeps the row
+  first_order_terms    hand-worked first-order cases in tests/golden; the
+                       error against exact attention falls as eps^2 when the
+                       keys lie within eps of their block mean (the
+                       zeroth-order error as eps); the denominator term
+                       vanishes; block-constant keys and beta = -inf leave
+                       the output unchanged
+  kv_moments           n_j times numpy's cross-covariance (np.cov, bias=True);
+                       scale * q^T C_j equals first_order_terms' numerator
 No function here is "parity unpinned".
 """
 
@@ -266,7 +275,7 @@ def select_streaming(q: np.ndarray, kbar: np.ndarray, tau: np.ndarray,
 
 def forward_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, kbar: np.ndarray,
                   vhat: np.ndarray, sel_row: np.ndarray, i: int, block: int, scale: float,
-                  exact_only: bool = False) -> np.ndarray:
+                  exact_only: bool = False, first_order: bool = False) -> np.ndarray:
     """Output rows of query block i, O_i = N_i / D_i row by row (Eqs. 9-10).
 
     For a query token r of block i:
@@ -282,7 +291,13 @@ def forward_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, kbar: np.ndarray,
     approximate only; the ragged last block weighs n_j.  exact_only drops the
     approximate terms (plain keep-or-drop sparse attention, the page's
     exact-only comparison); a row with nothing selected then outputs 0.
+    first_order keeps the next term of the same expansion for every
+    unselected block (see first_order_terms); it needs the zeroth-order term
+    and is refused together with exact_only.
     """
+    if exact_only and first_order:
+        raise ValueError("the first-order term extends the zeroth-order approximation; "
+                         "it has no meaning in exact-only mode")
     L, d = q.shape
     nj = block_sizes(L, block).astype(F64)
     a, b = block_range(L, block, i)
@@ -303,11 +318,60 @@ def forward_block(q: np.ndarray, k: np.ndarray, v: np.ndarray, kbar: np.ndarray,
     pa = np.exp(ap - M)
     D = pe.sum(axis=1) + (pa * nj[U][None, :]).sum(axis=1)
     Num = pe @ np.asarray(v[keys], F64) + pa @ vhat[U]
+    if first_order:
+        for u, j in enumerate(U):
+            ka, kb = block_range(L, block, j)
+            num1, den1 = first_order_terms(qi, k[ka:kb], v[ka:kb], ap[:, u], M[:, 0], scale)
+            Num += num1
+            D += den1
     return Num / D[:, None]
 
 
+def first_order_terms(qi: np.ndarray, kj: np.ndarray, vj: np.ndarray, centre: np.ndarray,
+                      ref_max: np.ndarray, scale: float):
+    """First-order terms of one unselected block j for the query rows qi.
+
+    The page expands the block's exponential score matrix exp(S_ij), with
+    S_ij = scale * q_r . k_t (rows r of block i, keys t of block j), around
+    the row-wise mean score c_r = scale * q_r . Kbar_j broadcast along the
+    keys: exp(S_ij) = exp(c) (1 + (S_ij - c) + ...), element-wise.  The
+    zeroth-order term is what forward_block already adds.  The first-order
+    term is exp(c_r) (S_rt - c_r); entering the numerator with the keys'
+    values and the denominator with weight 1 per key, it gives, relative to
+    the reference max ref_max_r,
+        numerator   exp(c_r - ref_max_r) * sum_t (S_rt - c_r) v_t
+        denominator exp(c_r - ref_max_r) * sum_t (S_rt - c_r)
+    The denominator term is zero up to rounding, because c_r is the mean of
+    S_rt over the block's keys; it is computed here all the same, from the
+    definition, and the tests check that it vanishes.
+    Returns (numerator terms n_i x d, denominator terms n_i).
+    """
+    S = scale * (np.asarray(qi, F64) @ np.asarray(kj, F64).T)   # n_i x n_j
+    x = S - centre[:, None]
+    w = np.exp(centre - ref_max)
+    return w[:, None] * (x @ np.asarray(vj, F64)), w * x.sum(axis=1)
+
+
+def kv_moments(k: np.ndarray, v: np.ndarray, block: int) -> np.ndarray:
+    """Per-block key-value moments of the first-order term, N x d x d:
+    C_j = sum over block j's valid tokens t of (k_t - Kbar_j) v_t^T, i.e. n_j
+    times the block's key-value cross-covariance.  With it the first-order
+    numerator term of first_order_terms is exp(c_r - ref_max_r) * scale *
+    q_r^T C_j, with no pass over the block's keys; the kernels use this form.
+    """
+    L, d = k.shape
+    N = num_blocks(L, block)
+    out = np.zeros((N, d, d), F64)
+    for j in range(N):
+        a, b = block_range(L, block, j)
+        kj = np.asarray(k[a:b], F64)
+        out[j] = (kj - kj.mean(axis=0)).T @ np.asarray(v[a:b], F64)
+    return out
+
+
 def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray,
-            block: int, scale: float, exact_only: bool = False) -> np.ndarray:
+            block: int, scale: float, exact_only: bool = False,
+            first_order: bool = False) -> np.ndarray:
     """Output of every query block for a given selection (see forward_block)."""
     L, d = q.shape
     N = num_blocks(L, block)
@@ -315,7 +379,8 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray,
     out = np.zeros((L, d), F64)
     for i in range(N):
         a, b = block_range(L, block, i)
-        out[a:b] = forward_block(q, k, v, kbar, vhat, sel[i], i, block, scale, exact_only)
+        out[a:b] = forward_block(q, k, v, kbar, vhat, sel[i], i, block, scale, exact_only,
+                                 first_order)
     return out
 
 
@@ -394,7 +459,8 @@ class HeadResult:
 
 def solattn_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float, block: int,
                  scale: Optional[float] = None, sel: Optional[np.ndarray] = None,
-                 exact_only: bool = False, rows: Optional[np.ndarray] = None) -> HeadResult:
+                 exact_only: bool = False, rows: Optional[np.ndarray] = None,
+                 first_order: bool = False) -> HeadResult:
     """Pool, moments, thresholds, selection and output for one head.
 
     sel, if given, forces the selection (used to compare outputs when a GPU
@@ -412,23 +478,26 @@ def solattn_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, beta: float, block
     free_sel = select(shat, tau)
     use = free_sel if sel is None else np.asarray(sel, bool)
     if rows is None:
-        out = forward(q, k, v, use, block, scale, exact_only)
+        out = forward(q, k, v, use, block, scale, exact_only, first_order)
     else:
         out = np.full((L, d), np.nan)
         for i in rows:
             a, b = block_range(L, block, int(i))
             out[a:b] = forward_block(q, k, v, kbar, vhat, use[int(i)], int(i), block, scale,
-                                     exact_only)
+                                     exact_only, first_order)
     return HeadResult(qbar=qbar, kbar=kbar, vhat=vhat, m=m, cov=cov, mu=mu, sigma=sigma,
                       tau=tau, shat=shat, sel=free_sel, used_sel=use, out=out, scale=scale)
 
 
-def executed_flops(L: int, d: int, block: int, sel: np.ndarray, exact_only: bool = False) -> float:
+def executed_flops(L: int, d: int, block: int, sel: np.ndarray, exact_only: bool = False,
+                   first_order: bool = False) -> float:
     """Algorithmic FLOPs of the fused pass on one head for a given selection.
 
     Per query block i: 4 n_i n_j d for each selected block (Q K^T and P V),
     2 n_i d N for the token-to-block score tile, 2 n_i d |U_i| for the
-    approximate P Vhat product.  Valid tokens only.
+    approximate P Vhat product.  Valid tokens only.  With first_order, also
+    2 n_i d^2 |U_i| for the products q_r^T C_j and 2 L d^2 for the moments
+    C_j themselves.
     """
     nj = block_sizes(L, block).astype(F64)
     N = len(nj)
@@ -436,4 +505,7 @@ def executed_flops(L: int, d: int, block: int, sel: np.ndarray, exact_only: bool
     exact = 4.0 * d * (nj[:, None] * nj[None, :] * s).sum()
     tile = 2.0 * d * nj.sum() * N
     approx = 0.0 if exact_only else 2.0 * d * (nj * (~s).sum(axis=1)).sum()
-    return float(exact + tile + approx)
+    first = 0.0
+    if first_order:
+        first = 2.0 * d * d * (nj * (~s).sum(axis=1)).sum() + 2.0 * d * d * L
+    return float(exact + tile + approx + first)

@@ -222,7 +222,9 @@ def test_hand_worked_example():
     ev = lambda s: float(eval(s, env, {"e": math.e, "inf": math.inf}))
     for case in g["cases"]:
         beta = ev(case["beta"])
-        r = ref.solattn_head(q, k, v, beta, block, scale=scale, exact_only=case["exact_only"])
+        first = case.get("first_order", False)
+        r = ref.solattn_head(q, k, v, beta, block, scale=scale, exact_only=case["exact_only"],
+                             first_order=first)
         np.testing.assert_allclose(r.mu, [ev(x) for x in g["mu"]], rtol=1e-14)
         np.testing.assert_allclose(r.sigma, [ev(x) for x in g["sigma"]], rtol=1e-14)
         if "tau" in case:
@@ -230,7 +232,7 @@ def test_hand_worked_example():
         np.testing.assert_array_equal(r.sel, np.array(case["selected"]))
         want = np.array([[ev(x) for x in row] for row in case["out"]])
         np.testing.assert_allclose(r.out, want, rtol=1e-13)
-        if not case["exact_only"]:
+        if not case["exact_only"] and not first:
             out_s, _ = ref.forward_streaming(q, k, v, r.tau, block, 1, scale)
             np.testing.assert_allclose(out_s, want, rtol=1e-13)
 
@@ -321,3 +323,121 @@ def test_topp_special_cases():
     assert ref.select_topp(_rows(3), 1.0).all()
     with pytest.raises(ValueError):
         ref.select_topp(row, 0.0)
+
+
+# ---------------------------------------------------------------- first-order term
+# The next term of the page's Taylor expansion of an unselected block's
+# exponential scores around the block's row-wise mean score.
+
+def _near_mean_keys(L, d, block, eps, seed=3):
+    """Keys within eps of their block mean: k_t = Kbar_j + eps delta_t with the
+    deltas of each block centred, so Kbar_j does not depend on eps."""
+    rng = np.random.default_rng(seed)
+    N = ref.num_blocks(L, block)
+    base = rng.standard_normal((N, d))
+    delta = rng.standard_normal((L, d))
+    k = np.empty((L, d))
+    for j in range(N):
+        a, b = ref.block_range(L, block, j)
+        k[a:b] = base[j] + eps * (delta[a:b] - delta[a:b].mean(axis=0))
+    q = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    return q, k, v
+
+
+def test_first_order_error_is_second_order_in_the_key_spread():
+    # All blocks approximated (beta = +inf).  Exact attention differs from
+    # the zeroth-order output by O(eps) and from the first-order output by
+    # O(eps^2): halving eps halves the one error and quarters the other.
+    # A dropped scale, a sign error or a transposed moment breaks the eps^2.
+    L, d, block = 45, 6, 8   # ragged last block of 5 tokens
+    N = ref.num_blocks(L, block)
+    none = np.zeros((N, N), bool)
+    scale = 0.5
+    errs0, errs1 = [], []
+    for eps in (0.02, 0.01, 0.005):
+        q, k, v = _near_mean_keys(L, d, block, eps)
+        exact = ref.dense(q, k, v, scale)
+        errs0.append(np.abs(ref.forward(q, k, v, none, block, scale) - exact).max())
+        errs1.append(np.abs(ref.forward(q, k, v, none, block, scale, first_order=True)
+                            - exact).max())
+    for a, b in zip(errs0, errs0[1:]):
+        assert 1.8 < a / b < 2.2, errs0
+    for a, b in zip(errs1, errs1[1:]):
+        assert 3.6 < a / b < 4.4, errs1
+    assert errs1[-1] < 0.05 * errs0[-1]
+
+
+def test_first_order_denominator_term_vanishes():
+    _, q, k, v = small(L=300, d=16, block=64, kind="pos", grid=(1, 1, 300))
+    qi = np.asarray(q[64:128], np.float64)
+    kj, vj = np.asarray(k[128:192], np.float64), np.asarray(v[128:192], np.float64)
+    scale = 0.25
+    centre = scale * (qi @ kj.mean(axis=0))
+    num, den = ref.first_order_terms(qi, kj, vj, centre, centre.max() * np.ones(64), scale)
+    S = scale * (qi @ kj.T)
+    size = (np.exp(centre - centre.max())[:, None] * np.abs(S - centre[:, None])).sum(axis=1)
+    assert np.all(np.abs(den) <= 1e-13 * size)
+    assert np.abs(num).max() > 1e-3
+
+
+def test_kv_moments_is_n_times_numpy_cross_covariance():
+    L, d, block = 150, 5, 64
+    _, _, k, v = small(L=L, d=d, block=block)
+    C = ref.kv_moments(k, v, block)
+    for j in range(ref.num_blocks(L, block)):
+        a, b = ref.block_range(L, block, j)
+        cov = np.cov(np.asarray(k[a:b], np.float64).T, np.asarray(v[a:b], np.float64).T,
+                     bias=True)[:d, d:]
+        np.testing.assert_allclose(C[j], (b - a) * cov, rtol=1e-11, atol=1e-12)
+
+
+def test_kv_moments_give_the_first_order_numerator():
+    # scale * q_r^T C_j (the moment form the kernels use) equals the token
+    # form sum_t (S_rt - c_r) v_t of first_order_terms.
+    L, d, block = 200, 12, 64
+    _, q, k, v = small(L=L, d=d, block=block, kind="pos", grid=(1, 1, L))
+    scale = 0.3
+    C = ref.kv_moments(k, v, block)
+    qi = np.asarray(q[:64], np.float64)
+    for j in range(ref.num_blocks(L, block)):
+        a, b = ref.block_range(L, block, j)
+        centre = scale * (qi @ np.asarray(k[a:b], np.float64).mean(axis=0))
+        num, _ = ref.first_order_terms(qi, k[a:b], v[a:b], centre, centre, scale)
+        np.testing.assert_allclose(num, scale * (qi @ C[j]), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("beta", [-math.inf, 0.0, 1.0, math.inf])
+def test_first_order_with_block_constant_keys_is_dense(beta):
+    # Constant keys within each block make S - c = 0: the first-order term
+    # adds nothing and the output is still dense attention.
+    rng = np.random.default_rng(8)
+    L, d, block = 200, 8, 64
+    N = ref.num_blocks(L, block)
+    kb = rng.standard_normal((N, d))
+    k = np.repeat(kb, block, axis=0)[:L]
+    q = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    r = ref.solattn_head(q, k, v, beta, block, first_order=True)
+    np.testing.assert_allclose(r.out, sdpa(q, k, v, r.scale), rtol=1e-10, atol=1e-12)
+
+
+def test_first_order_at_beta_minus_inf_is_dense():
+    w, q, k, v = small(L=300, d=16, block=64, kind="pos", grid=(1, 1, 300))
+    r = ref.solattn_head(q, k, v, -math.inf, 64, first_order=True)
+    np.testing.assert_allclose(r.out, sdpa(q, k, v, r.scale), rtol=1e-10, atol=1e-12)
+
+
+def test_first_order_refuses_exact_only():
+    _, q, k, v = small(L=100, d=8, block=64)
+    with pytest.raises(ValueError):
+        ref.solattn_head(q, k, v, 1.0, 64, exact_only=True, first_order=True)
+
+
+def test_first_order_flops():
+    L, d, b = 1000, 64, 64
+    N = ref.num_blocks(L, b)
+    none = np.zeros((N, N), bool)
+    base = ref.executed_flops(L, d, b, none)
+    assert ref.executed_flops(L, d, b, none, first_order=True) == \
+        base + 2.0 * d * d * L * N + 2.0 * d * d * L
