@@ -103,6 +103,9 @@ struct AttnArgs {
   uint64_t* sel_mask;
   int32_t* sel_count;
   const uint64_t* sel_in;  // given selections (masked mode) or null (threshold routing)
+  float* out_f32;          // if set: O in float32 here instead of bf16 in out
+  float* lse2;             // if set: per row, log2 of the softmax denominator in logit units
+                           // (m + log2 l, the scale of the 2^(c s - m) weights)
   int64_t L;
   uint32_t N;
   uint32_t pairs;    // ceil(N / 2)
@@ -114,22 +117,6 @@ struct AttnArgs {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Wait until at most N of this wave's vector-memory loads are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// s_waitcnt vmcnt(0) issued through the builtin, so that the compiler's own
-// waitcnt bookkeeping sees it: loads issued before it (the Q operand, the
-// routing inputs) count as complete inside the block loop, which then needs
-// no vector-memory wait of the compiler's own.  Encoding (gfx9): vmcnt 0,
-// expcnt 7, lgkmcnt 15.
-__device__ __forceinline__ void settle_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// Workgroup barrier that does not wait for outstanding direct-to-LDS loads.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // The running max is only raised when a score exceeds it by more than
 // 2^kLazyRescale (log2 units); below that, probabilities up to 2^8 simply
@@ -196,12 +183,9 @@ struct TileDma {
       voff[c] = offset(row, lane, true);
     }
   }
-  // The s_nop covers the M0-write to LDS-DMA hazard.
   __device__ __forceinline__ static void load(uint32_t voffset, const uint16_t* sbase,
                                               uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(sbase),
-                 "{m0}"(lds)
-                 : "memory");
+    lds_dma_16b(voffset, sbase, lds);
   }
   // K and V of key block j (nkeys valid rows) into the tiles at LDS byte
   // addresses lds_k / lds_v.  Rows >= nkeys re-read row nkeys - 1 (finite
@@ -235,11 +219,6 @@ struct TileDma {
   }
 };
 
-// LDS byte address of a __shared__ object (wave-uniform).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
-}
 
 // Per-lane byte offsets, within a tile, of this lane's MFMA operand reads.
 // They do not depend on the 32-key tile mt or the P V k-step kk (the
@@ -825,7 +804,22 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   // O = N / D: combine the two lane halves of the denominator.
   const float ltot = l_run + __shfl_xor(l_run, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (qrow < n_i) {
+  if (a.lse2 != nullptr && qrow < n_i && h == 0)
+    a.lse2[(size_t)bh * L + (size_t)i_g * BLK + qrow] = m_run + __builtin_amdgcn_logf(ltot);
+  if (a.out_f32 != nullptr) {
+    if (qrow < n_i) {
+      float* orow = a.out_f32 + head + ((size_t)i_g * BLK + qrow) * D;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 st;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st[e] = o[dt][4 * r4 + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * r4 + 4 * h) = st;
+        }
+    }
+  } else if (qrow < n_i) {
     uint16_t* orow = a.out + head + ((size_t)i_g * BLK + qrow) * D;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -874,7 +868,7 @@ int64_t fused_max_blocks() { return kMaxBlocks; }
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,
                       const uint64_t* sel_in, void* out, uint64_t* sel_mask, int32_t* sel_count,
-                      hipStream_t stream) {
+                      float* out_f32, float* lse2, hipStream_t stream) {
   AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -887,6 +881,8 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
   a.sel_mask = sel_mask;
   a.sel_count = sel_count;
   a.sel_in = sel_in;
+  a.out_f32 = out_f32;
+  a.lse2 = lse2;
   a.exact_only = (s.flags & 1u) ? 1u : 0u;
   return launch_attn<true>(s, a, stream);
 }

@@ -77,6 +77,44 @@ __device__ __forceinline__ constexpr int mfma_row(int r, int h) {
   return 8 * (r / 4) + 4 * h + (r % 4);
 }
 
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(0) issued through the builtin, so that the compiler's own
+// waitcnt bookkeeping sees it: loads issued before it (the Q operand and
+// other set-up loads) count as complete inside a block loop, which then
+// needs no vector-memory wait of the compiler's own.  Encoding (gfx9):
+// vmcnt 0, expcnt 7, lgkmcnt 15.
+__device__ __forceinline__ void settle_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier that does not wait for outstanding direct-to-LDS loads.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+
+// Direct-to-LDS load (global_load_lds_dwordx4): each lane fetches 16 bytes
+// at sbase + voffset and the wave writes them to 1 KB of LDS at
+// lds + 16 * lane.  sbase and lds must be wave-uniform.  Issued from inline
+// assembly, so the compiler does not count it: the caller waits for it
+// (wait_vm) before a barrier that publishes the data.  The s_nop covers the
+// M0-write to LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma_16b(uint32_t voffset, const uint16_t* sbase,
+                                            uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voffset), "s"(sbase),
+               "{m0}"(lds)
+               : "memory");
+}
+
 __device__ __forceinline__ float wave_max_pair(float x) {
   // lanes l and l^32 hold the two halves of one 32x32 result column
   return fmaxf(x, __shfl_xor(x, 32));

@@ -29,11 +29,23 @@ hipError_t launch_moments(const Shape& s, const float* qbar, const float* kbar, 
 int64_t fused_max_blocks();
 
 // sel_in null: threshold routing from qbar and tau.  Otherwise the given
-// selections (qbar and tau unused).
+// selections (qbar and tau unused).  out_f32, if set, receives O in float32
+// instead of out; lse2, if set, the log2 of each row's softmax denominator in
+// units of scale * log2(e) * q.k (f32 [bh, L]).
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,
                       const uint64_t* sel_in, void* out, uint64_t* sel_mask, int32_t* sel_count,
-                      hipStream_t stream);
+                      float* out_f32, float* lse2, hipStream_t stream);
+
+// First-order term of the unselected blocks.
+// kvc[bh][j][b][a] = sum over block j's valid tokens t of v_t[b] (k_t[a] - Kbar_j[a]), bf16.
+hipError_t launch_kv_moments(const Shape& s, const void* k, const void* v, const float* kbar,
+                             void* kvc, hipStream_t stream);
+// out = bf16(o32 + sum over j unselected (sel_mask) of 2^(c q.Kbar_j - lse2) scale C_j^T q)
+// row by row; o32, lse2 and sel_mask as written by launch_fwd.
+hipError_t launch_first_order(const Shape& s, const void* q, const float* kbar, const void* kvc,
+                              const uint64_t* sel_mask, const float* lse2, const float* o32,
+                              void* out, hipStream_t stream);
 
 hipError_t launch_dense(const Shape& s, const void* q, const void* k, const void* v, void* out,
                         hipStream_t stream);

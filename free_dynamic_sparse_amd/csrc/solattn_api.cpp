@@ -52,6 +52,24 @@ int check_routing(const solattn_problem_t* p) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? SOLATTN_OK : SOLATTN_E_HIP; }
 
+// Regions of the first-order workspace, each starting on a 256-byte boundary:
+// the fused kernel's selection bitmaps (u64 [bh, N, ceil(N/64)]), its per-row
+// log2 denominators (f32 [bh, L]) and its float32 output (f32 [bh, L, d]).
+struct FirstOrderLayout {
+  size_t sel, lse2, o32, total;
+};
+
+FirstOrderLayout first_order_layout(const solattn::Shape& s) {
+  auto up = [](size_t x) { return (x + 255u) & ~(size_t)255u; };
+  const size_t w64 = (size_t)((s.N + 63) / 64);
+  FirstOrderLayout l;
+  l.sel = 0;
+  l.lse2 = up((size_t)s.bh * (size_t)s.N * w64 * 8u);
+  l.o32 = l.lse2 + up((size_t)s.bh * (size_t)s.L * 4u);
+  l.total = l.o32 + up((size_t)s.bh * (size_t)s.L * (size_t)s.d * 4u);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,7 +119,8 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
       !ok_opt_ptr(sel_count))
     return SOLATTN_E_INVALID_ARG;
   return from_hip(solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, nullptr, out, sel_mask,
-                                      sel_count, static_cast<hipStream_t>(stream)));
+                                      sel_count, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k, const void* v,
@@ -117,7 +136,56 @@ int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k,
       !ok_ptr(sel_in) || !ok_ptr(out))
     return SOLATTN_E_INVALID_ARG;
   return from_hip(solattn::launch_fwd(s, q, k, v, nullptr, kbar, vhat, nullptr, sel_in, out,
-                                      nullptr, nullptr, static_cast<hipStream_t>(stream)));
+                                      nullptr, nullptr, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int solattn_kv_moments(const solattn_problem_t* p, const void* k, const void* v,
+                       const float* kbar, void* kvc, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(kbar) || !ok_ptr(kvc)) return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_kv_moments(s, k, v, kbar, kvc,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t solattn_fwd_first_order_workspace(const solattn_problem_t* p) {
+  solattn::Shape s;
+  bool empty = false;
+  if (check_shape(p, &s, &empty) != SOLATTN_OK || empty) return 0;
+  return first_order_layout(s).total;
+}
+
+int solattn_fwd_first_order(const solattn_problem_t* p, const void* q, const void* k,
+                            const void* v, const float* qbar, const float* kbar,
+                            const float* vhat, const void* kvc, const float* tau, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  rc = check_routing(p);
+  if (rc != SOLATTN_OK) return rc;
+  if (p->flags & SOLATTN_FLAG_EXACT_ONLY) return SOLATTN_E_INVALID_ARG;
+  if (s.N > solattn::fused_max_blocks()) return SOLATTN_E_UNSUPPORTED;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(qbar) || !ok_ptr(kbar) ||
+      !ok_ptr(vhat) || !ok_ptr(kvc) || !ok_ptr(tau) || !ok_ptr(out) || !ok_ptr(workspace))
+    return SOLATTN_E_INVALID_ARG;
+  const FirstOrderLayout l = first_order_layout(s);
+  if (workspace_bytes < l.total) return SOLATTN_E_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  uint64_t* sel = reinterpret_cast<uint64_t*>(ws + l.sel);
+  float* lse2 = reinterpret_cast<float*>(ws + l.lse2);
+  float* o32 = reinterpret_cast<float*>(ws + l.o32);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, nullptr, nullptr, sel,
+                                     nullptr, o32, lse2, st);
+  if (e != hipSuccess) return SOLATTN_E_HIP;
+  return from_hip(solattn::launch_first_order(s, q, kbar, kvc, sel, lse2, o32, out, st));
 }
 
 int solattn_dense_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
@@ -178,7 +246,8 @@ const char* solattn_strerror(int code) {
       return "ok";
     case SOLATTN_E_INVALID_ARG:
       return "invalid argument (null or misaligned pointer, bad shape, NaN beta or scale, "
-             "k < 1, top_p outside (0, 1])";
+             "k < 1, top_p outside (0, 1], a first-order workspace too small, or the "
+             "first-order forward asked for in exact-only mode)";
     case SOLATTN_E_UNSUPPORTED:
       return "unsupported configuration (head_dim and block must be 64 or 128, chunk 1..64, "
              "and solattn_fwd and the top-k / top-p selections need ceil(seq_len / block) "
@@ -190,6 +259,6 @@ const char* solattn_strerror(int code) {
   }
 }
 
-int solattn_version(void) { return 100; }
+int solattn_version(void) { return 200; }
 
 }  // extern "C"

@@ -27,6 +27,7 @@ SOLATTN_FLAG_EXACT_ONLY = 1
 EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_masked",
            "solattn_dense_fwd",
            "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp",
+           "solattn_kv_moments", "solattn_fwd_first_order", "solattn_fwd_first_order_workspace",
            "solattn_strerror", "solattn_version")
 
 
@@ -61,8 +62,14 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.solattn_proxy_map.argtypes = [pp, vp, vp, vp, vp]
     lib.solattn_select_topk.argtypes = [pp, vp, ctypes.c_int64, vp, vp, vp]
     lib.solattn_select_topp.argtypes = [pp, vp, ctypes.c_float, vp, vp, vp]
+    lib.solattn_kv_moments.argtypes = [pp, vp, vp, vp, vp, vp]
+    lib.solattn_fwd_first_order_workspace.argtypes = [pp]
+    lib.solattn_fwd_first_order_workspace.restype = ctypes.c_size_t
+    lib.solattn_fwd_first_order.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.c_size_t, vp]
     for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_masked",
-                 "solattn_dense_fwd", "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp"):
+                 "solattn_dense_fwd", "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp",
+                 "solattn_kv_moments", "solattn_fwd_first_order"):
         getattr(lib, name).restype = ctypes.c_int
     lib.solattn_strerror.argtypes = [ctypes.c_int]
     lib.solattn_strerror.restype = ctypes.c_char_p
@@ -174,6 +181,40 @@ def solattn_fwd_masked(p: Problem, q, k, v, kbar, vhat, sel_in, out, stream=None
            "solattn_fwd_masked")
 
 
+def solattn_kv_moments(p: Problem, k, v, kbar, kvc, stream=None) -> None:
+    full, pooled, N = _dims(p)
+    _need(k, torch.bfloat16, full, "k")
+    _need(v, torch.bfloat16, full, "v")
+    _need(kbar, torch.float32, pooled, "kbar")
+    _need(kvc, torch.bfloat16, (p.batch, p.heads, N, p.head_dim, p.head_dim), "kvc")
+    _check(LIB.solattn_kv_moments(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(kbar), _ptr(kvc),
+                                  _stream(stream)), "solattn_kv_moments")
+
+
+def solattn_fwd_first_order_workspace(p: Problem) -> int:
+    return int(LIB.solattn_fwd_first_order_workspace(ctypes.byref(p)))
+
+
+def solattn_fwd_first_order(p: Problem, q, k, v, qbar, kbar, vhat, kvc, tau, out, workspace,
+                            stream=None) -> None:
+    """workspace: a contiguous uint8 CUDA tensor of at least
+    solattn_fwd_first_order_workspace(p) bytes."""
+    full, pooled, N = _dims(p)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, full, n)
+    for t, n in ((qbar, "qbar"), (kbar, "kbar"), (vhat, "vhat")):
+        _need(t, torch.float32, pooled, n)
+    _need(kvc, torch.bfloat16, (p.batch, p.heads, N, p.head_dim, p.head_dim), "kvc")
+    _need(tau, torch.float32, (p.batch, p.heads, N), "tau")
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_cuda \
+            or not workspace.is_contiguous():
+        raise ValueError("workspace: expected a contiguous 1-D uint8 CUDA tensor")
+    _check(LIB.solattn_fwd_first_order(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar),
+                                       _ptr(kbar), _ptr(vhat), _ptr(kvc), _ptr(tau), _ptr(out),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)),
+           "solattn_fwd_first_order")
+
+
 def solattn_dense_fwd(p: Problem, q, k, v, out, stream=None) -> None:
     full, _, _ = _dims(p)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
@@ -247,6 +288,40 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0
     solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma, stream)
     solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask, ws.sel_count,
                 stream)
+    return out
+
+
+class FirstOrderWorkspace:
+    """Device buffers of the first-order forward for one problem shape: the
+    block moments C_j and the scratch passed between its two kernels."""
+
+    def __init__(self, p: Problem, device="cuda"):
+        N = num_blocks(p.seq_len, p.block)
+        self.kvc = torch.empty((p.batch, p.heads, N, p.head_dim, p.head_dim),
+                               dtype=torch.bfloat16, device=device)
+        self.scratch = torch.empty(max(1, solattn_fwd_first_order_workspace(p)),
+                                   dtype=torch.uint8, device=device)
+
+
+def forward_first_order(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0,
+                        block: int = 128, chunk: int = 32, scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None,
+                        fws: Optional[FirstOrderWorkspace] = None, stream=None) -> torch.Tensor:
+    """The forward with the first-order term of every unselected block:
+    pool, moments/thresholds, block moments C_j, fused kernel, correction."""
+    B, H, L, d = q.shape
+    p = problem(B, H, L, d, block, chunk, beta, scale)
+    if ws is None:
+        ws = Workspace(p, q.device)
+    if fws is None:
+        fws = FirstOrderWorkspace(p, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, stream)
+    solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma, stream)
+    solattn_kv_moments(p, k, v, ws.kbar, fws.kvc, stream)
+    solattn_fwd_first_order(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, fws.kvc, ws.tau, out,
+                            fws.scratch, stream)
     return out
 
 

@@ -10,7 +10,9 @@
  * and solattn_dense_fwd is plain dense softmax attention on the same core,
  * kept as the in-house comparison point.  solattn_proxy_map with
  * solattn_select_topk / solattn_select_topp are the top-k and top-p routing
- * baselines the page compares its routing with.
+ * baselines the page compares its routing with.  solattn_kv_moments with
+ * solattn_fwd_first_order keep the first-order term of the expansion whose
+ * zeroth-order term the page uses for unselected blocks.
  *
  * Conventions shared by every entry point
  * - Tensors are contiguous row-major device memory.  Q, K, V and O are
@@ -158,6 +160,55 @@ int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k,
                        const float* kbar, const float* vhat, const uint64_t* sel_in, void* out,
                        void* stream);
 
+/*
+ * First-order term of the unselected blocks.  The page expands an
+ * unselected block's exponential score matrix exp(S_ij) around the
+ * row-wise mean score within the block, c_r = scale*q_r.Kbar_j, and keeps
+ * the zeroth-order term (method section, the expansion before Eqs. 9-10).
+ * The first-order term exp(c_r)*(S_rt - c_r) sums to zero over the block's
+ * keys, so the denominator is unchanged, and adds
+ * exp(c_r) * scale * q_r^T C_j to the numerator, with the block moment
+ *   C_j = sum over block j's valid tokens t of (k_t - Kbar_j) v_t^T  (d x d).
+ *
+ * solattn_kv_moments: C_j of every block.
+ *   k, v  in:  bf16 [B, H, L, d]
+ *   kbar  in:  f32 [B, H, N, d]  from solattn_pool
+ *   kvc   out: bf16 [B, H, N, d, d], value dimension first:
+ *              element [b][h][j][e][a] is C_j[a][e] (key dim a, value dim e)
+ * The centred keys k_t - Kbar_j are rounded to bf16 and the products
+ * accumulate in float32.  beta, chunk and flags are ignored.
+ *
+ * solattn_fwd_first_order: solattn_fwd (threshold routing, exact selected
+ * blocks, zeroth-order unselected blocks) with the first-order term of every
+ * unselected block added, so that row r of query block i is
+ *   O_r = (N_r + sum_{j in U_i} exp(c_rj) scale q_r^T C_j) / D_r
+ * with N_r and D_r the zeroth-order numerator and denominator (Eqs. 9-10).
+ *   q, k, v, qbar, kbar, vhat, tau, out  as for solattn_fwd
+ *   kvc        in: bf16 [B, H, N, d, d] from solattn_kv_moments
+ *   workspace  device scratch of workspace_bytes >=
+ *              solattn_fwd_first_order_workspace(p) bytes, 16-byte aligned;
+ *              its contents on entry do not matter and are overwritten (the
+ *              selection bitmaps, the per-row denominators and O in float32,
+ *              passed between the two kernels of the call)
+ * Two kernels: the fused forward writes float32 O, its log denominators and
+ * the bitmaps to the workspace; a second kernel adds the first-order terms
+ * (an MFMA product C_j^T q_r per query row and unselected block: 2 n_i d^2
+ * FLOPs per block pair) and rounds O to bf16 once.  Calls that share a
+ * workspace race.  SOLATTN_FLAG_EXACT_ONLY is refused
+ * (SOLATTN_E_INVALID_ARG): the first-order term extends the zeroth-order
+ * one.  A workspace smaller than required is SOLATTN_E_INVALID_ARG.  Same
+ * limit as solattn_fwd (N <= 8192).
+ *
+ * solattn_fwd_first_order_workspace: the workspace size in bytes; 0 for an
+ * empty or invalid problem.
+ */
+int solattn_kv_moments(const solattn_problem_t* p, const void* k, const void* v,
+                       const float* kbar, void* kvc, void* stream);
+size_t solattn_fwd_first_order_workspace(const solattn_problem_t* p);
+int solattn_fwd_first_order(const solattn_problem_t* p, const void* q, const void* k,
+                            const void* v, const float* qbar, const float* kbar,
+                            const float* vhat, const void* kvc, const float* tau, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 /*
  * Dense softmax attention softmax(scale * Q K^T) V on the same MFMA core,
  * block by block with one online softmax (no routing).  beta, chunk and

@@ -44,7 +44,7 @@ def test_problem_struct_layout_matches_header(sa):
 
 
 def test_version_and_strerror(sa):
-    assert sa.LIB.solattn_version() == 100
+    assert sa.LIB.solattn_version() == 200
     for code in (0, -1, -2, -3, 7):
         assert isinstance(sa.LIB.solattn_strerror(code), bytes)
 
@@ -178,3 +178,54 @@ def test_masked_forward_rejects_bad_arguments(sa):
     assert lib.solattn_fwd_masked(ctypes.byref(big), *([P(FAKE)] * 7), None) == -2
     empty = sa.problem(2, 0, 4096, 128, 128, 32, 1.0)
     assert lib.solattn_fwd_masked(ctypes.byref(empty), *([None] * 7), None) == 0
+
+
+def test_first_order_workspace_size(sa):
+    lib = sa.LIB
+    p = sa.problem(2, 3, 1000, 128, 128, 32, 1.0)   # N = 8, one bitmap word per row
+    up = lambda x: (x + 255) // 256 * 256
+    want = up(2 * 3 * 8 * 1 * 8) + up(2 * 3 * 1000 * 4) + up(2 * 3 * 1000 * 128 * 4)
+    assert lib.solattn_fwd_first_order_workspace(ctypes.byref(p)) == want
+    assert sa.solattn_fwd_first_order_workspace(p) == want
+    assert lib.solattn_fwd_first_order_workspace(ctypes.byref(sa.problem(0, 3, 1000, 128))) == 0
+    assert lib.solattn_fwd_first_order_workspace(ctypes.byref(sa.problem(1, 1, 1000, 96))) == 0
+    assert lib.solattn_fwd_first_order_workspace(None) == 0
+
+
+def test_first_order_entry_points_reject_bad_arguments(sa):
+    lib = sa.LIB
+    P = lambda x: ctypes.c_void_p(x)
+    p = sa.problem(1, 2, 4096, 128, 128, 32, 1.0)
+    need = lib.solattn_fwd_first_order_workspace(ctypes.byref(p))
+
+    def fo(prob, ptrs, size=need):
+        # ptrs: q, k, v, qbar, kbar, vhat, kvc, tau, out, workspace
+        return lib.solattn_fwd_first_order(ctypes.byref(prob), *ptrs, size, None)
+
+    for i in range(10):   # each pointer null, then misaligned
+        ptrs = [P(FAKE)] * 10
+        ptrs[i] = None
+        assert fo(p, ptrs) == -1, i
+        ptrs[i] = P(FAKE + 8)
+        assert fo(p, ptrs) == -1, i
+    ok = [P(FAKE)] * 10
+    assert fo(p, ok, need - 1) == -1                        # workspace too small
+    exact = sa.problem(1, 2, 4096, 128, 128, 32, 1.0, exact_only=True)
+    assert fo(exact, ok) == -1                              # exact-only is refused
+    nan = sa.problem(1, 2, 4096, 128, 128, 32, math.nan)
+    assert fo(nan, ok) == -1
+    big = sa.problem(1, 1, 128 * 8193, 128, 128, 32, 1.0)
+    assert fo(big, ok, 1 << 40) == -2
+    assert fo(sa.problem(1, 2, 4096, 96, 128, 32, 1.0), ok) == -2
+    empty = sa.problem(1, 0, 4096, 128, 128, 32, 1.0)
+    assert fo(empty, [None] * 10, 0) == 0
+    # kv moments: k, v, kbar, kvc
+    for i in range(4):
+        ptrs = [P(FAKE)] * 4
+        ptrs[i] = None
+        assert lib.solattn_kv_moments(ctypes.byref(p), *ptrs, None) == -1
+        ptrs[i] = P(FAKE + 8)
+        assert lib.solattn_kv_moments(ctypes.byref(p), *ptrs, None) == -1
+    assert lib.solattn_kv_moments(ctypes.byref(empty), None, None, None, None, None) == 0
+    assert lib.solattn_kv_moments(ctypes.byref(sa.problem(1, 1, 64, 128, 32)),
+                                  *[P(FAKE)] * 4, None) == -2
