@@ -177,6 +177,75 @@ def accuracy_study(sa, w: synth.Workload, betas=(0.0, 0.5, 1.0, 1.5, 2.0, 3.0, m
             "rows": rows}
 
 
+def first_order_study(sa, w: synth.Workload, betas=(0.5, 1.0, 1.5, math.inf)):
+    """The first-order term of the unselected blocks against the page's
+    zeroth-order approximation and exact-only attention, at identical
+    selections (all three route the same way): error against dense attention
+    and time per call.  The first-order call is pool + moments + the block
+    moments C_j + the fused kernel (float32 output) + the correction kernel;
+    its extra MFMA work is 2 n_i d^2 FLOPs per (query block, unselected block)
+    plus 2 L d^2 per head for the moments."""
+    q, k, v = _to_device(w)
+    B, H, L, d = q.shape
+    dense = torch.empty_like(q)
+    out = torch.empty_like(q)
+    pd = sa.problem(B, H, L, d, w.block, w.chunk, -math.inf)
+    dense_ms = _time_ms(lambda: sa.solattn_dense_fwd(pd, q, k, v, dense), 2)
+    nj = torch.full((w.N,), float(w.block), dtype=torch.float64)
+    nj[-1] = float(L - (w.N - 1) * w.block)
+    rows = []
+    for beta in betas:
+        row = {"beta": beta if math.isfinite(beta) else str(beta)}
+        p = sa.problem(B, H, L, d, w.block, w.chunk, beta)
+        ws = sa.Workspace(p, debug=True)
+        fws = sa.FirstOrderWorkspace(p)
+
+        def zeroth():
+            sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
+            sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
+            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out)
+
+        def first():
+            sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
+            sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
+            sa.solattn_kv_moments(p, k, v, ws.kbar, fws.kvc)
+            sa.solattn_fwd_first_order(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, fws.kvc, ws.tau,
+                                       out, fws.scratch)
+
+        sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
+        sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
+        sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+                       ws.sel_count)
+        torch.cuda.synchronize()
+        unsel = (w.N - ws.sel_count.double().cpu()).reshape(B * H, w.N)
+        row["density"] = float(ws.sel_count.double().mean().item()) / w.N
+        row["first_order_tflop"] = float(2.0 * d * d * ((unsel * nj).sum() + B * H * L)) / 1e12
+        for mode, fn in (("zeroth_order", zeroth), ("first_order", first)):
+            fn()
+            torch.cuda.synchronize()
+            rel, cos = _errors(out, dense)
+            row[mode] = {"rel_l2_mean": float(rel.mean()), "rel_l2_max": float(rel.max()),
+                         "cosine_mean": float(cos.mean()), "cosine_min": float(cos.min()),
+                         "ms_per_call": _time_ms(fn, 3)}
+        pe = sa.problem(B, H, L, d, w.block, w.chunk, beta, None, True)
+        sa.solattn_fwd(pe, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out)
+        torch.cuda.synchronize()
+        rel, cos = _errors(out, dense)
+        row["exact_only"] = {"rel_l2_mean": float(rel.mean()), "cosine_mean": float(cos.mean())}
+        extra_ms = row["first_order"]["ms_per_call"] - row["zeroth_order"]["ms_per_call"]
+        row["first_order_extra_ms"] = extra_ms
+        row["first_order_extra_tflops"] = row["first_order_tflop"] / (extra_ms * 1e-3)
+        row["dense_ms"] = dense_ms
+        row["first_order_speedup_vs_dense"] = dense_ms / row["first_order"]["ms_per_call"]
+        rows.append(row)
+        log(f"first-order {row}")
+        del ws, fws
+        torch.cuda.empty_cache()
+    return {"study": "first_order", "workload": f"{w.name}: B{B} H{H} L{L} d{d} block{w.block} "
+            f"C{w.chunk}", "reference": "solattn_dense_fwd (bf16 output)", "data": "synthetic",
+            "rows": rows}
+
+
 SEQ_BETAS = (0.5, 1.0, 1.5, 2.0)
 
 
@@ -333,13 +402,16 @@ def main() -> int:
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--study", choices=("accuracy", "seq", "routing"), default=None,
+    ap.add_argument("--study", choices=("accuracy", "seq", "routing", "first-order"),
+                    default=None,
                     help="instead of the headline line, print one JSON line for a study: "
                          "'accuracy' (error against dense attention and cost of the "
                          "approximation, full vs exact-only, over beta), 'seq' (speedup over "
-                         "the dense kernel across sequence length and sparsity) or 'routing' "
+                         "the dense kernel across sequence length and sparsity), 'routing' "
                          "(selection latency, memory and per-row density spread of threshold "
-                         "routing against top-k and top-p over the proxy map)")
+                         "routing against top-k and top-p over the proxy map) or "
+                         "'first-order' (error and cost of adding the first-order term of "
+                         "the unselected blocks)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (for scaling "
                          "rocprofv3 byte counters) and exit")
@@ -370,6 +442,9 @@ def main() -> int:
         return 0
     if args.study == "seq":
         print(json.dumps(seq_study(sa)), flush=True)
+        return 0
+    if args.study == "first-order":
+        print(json.dumps(first_order_study(sa, synth.WORKLOADS[args.workload])), flush=True)
         return 0
     if args.study == "routing":
         print(json.dumps(routing_study(sa, synth.WORKLOADS[args.workload], args.beta)),
