@@ -398,6 +398,9 @@ def main() -> int:
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--block", type=int, default=0,
                     help="tokens per block (64 or 128); default: the workload's own (128)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="heads of the workload to run (default: all of them); e.g. 5 of "
+                         "Wan's 40 is one GPU's share when heads are split over eight")
     ap.add_argument("--beta", type=float, default=1.0)
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--skip-sweep", action="store_true")
@@ -454,6 +457,8 @@ def main() -> int:
     w = synth.WORKLOADS[args.workload]
     if args.block:
         w = w.replace(block=args.block)
+    if args.heads:
+        w = w.replace(H=args.heads)
     t0 = time.time()
     qb, kb, vb = synth.make_inputs_bf16_bits(w)
     dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
@@ -508,7 +513,8 @@ def main() -> int:
         return dict(wall_ms=wall * 1e3 / steps, pool_ms=float(np.mean(pool)),
                     moments_ms=float(np.mean(mom)), fwd_ms=float(np.mean(fwd)),
                     total_ms=float(np.mean(tot)), fwd_min_ms=float(np.min(fwd)),
-                    total_min_ms=float(np.min(tot)))
+                    total_min_ms=float(np.min(tot)), fwd_median_ms=float(np.median(fwd)),
+                    total_median_ms=float(np.median(tot)))
 
     beta = args.beta
     sel = selection(beta)
@@ -544,6 +550,7 @@ def main() -> int:
                    "beta": beta, "global_batch": B, "seq_len": L, "parallelism": "none"},
         "stages_ms": {"pool": t["pool_ms"], "moments": t["moments_ms"], "fwd": t["fwd_ms"],
                       "fwd_min": t["fwd_min_ms"], "total_min": t["total_min_ms"],
+                      "fwd_median": t["fwd_median_ms"], "total_median": t["total_median_ms"],
                       "host_wall_per_step": t["wall_ms"]},
         "density": density,
         "executed_tflop": fwd_flops / 1e12,
@@ -555,8 +562,8 @@ def main() -> int:
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      # counters were taken on the default workload only
-                     "traffic": measured_traffic() if (w.name, w.block, beta) == ("wan", 128, 1.0)
-                     else None},
+                     "traffic": measured_traffic()
+                     if (w.name, w.block, w.H, beta) == ("wan", 128, 40, 1.0) else None},
     }
 
     if not args.skip_dense:
