@@ -208,7 +208,7 @@ def first_order_study(sa, w: synth.Workload, betas=(0.5, 1.0, 1.5, math.inf)):
         def first():
             sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
             sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
-            sa.solattn_kv_moments(p, k, v, ws.kbar, fws.kvc)
+            sa.solattn_kv_moments(p, k, v, ws.kbar, ws.vhat, fws.kvc)
             sa.solattn_fwd_first_order(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, fws.kvc, ws.tau,
                                        out, fws.scratch)
 
@@ -226,12 +226,14 @@ def first_order_study(sa, w: synth.Workload, betas=(0.5, 1.0, 1.5, math.inf)):
             rel, cos = _errors(out, dense)
             row[mode] = {"rel_l2_mean": float(rel.mean()), "rel_l2_max": float(rel.max()),
                          "cosine_mean": float(cos.mean()), "cosine_min": float(cos.min()),
+                         "rel_l2_per_head": [round(float(x), 5) for x in rel],
                          "ms_per_call": _time_ms(fn, 3)}
         pe = sa.problem(B, H, L, d, w.block, w.chunk, beta, None, True)
         sa.solattn_fwd(pe, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out)
         torch.cuda.synchronize()
         rel, cos = _errors(out, dense)
-        row["exact_only"] = {"rel_l2_mean": float(rel.mean()), "cosine_mean": float(cos.mean())}
+        row["exact_only"] = {"rel_l2_mean": float(rel.mean()), "cosine_mean": float(cos.mean()),
+                             "rel_l2_per_head": [round(float(x), 5) for x in rel]}
         extra_ms = row["first_order"]["ms_per_call"] - row["zeroth_order"]["ms_per_call"]
         row["first_order_extra_ms"] = extra_ms
         row["first_order_extra_tflops"] = row["first_order_tflop"] / (extra_ms * 1e-3)

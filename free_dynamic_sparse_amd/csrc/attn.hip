@@ -25,10 +25,11 @@
 //     thresholds, and the decisions go to on-chip bitmaps (the page reads
 //     these scores off the token-to-block tile as column means: the same
 //     numbers, which a bf16 tile could not resolve inside the tie band); the
-//     same registers are stored to LDS as bf16 tiles (Kbar in the K layout,
-//     Vhat in the V layout), and the token-to-block tile scale * Q_i KC^T
-//     (MFMA) gives the logits of the unselected columns, which enter the
-//     group's online softmax with weight n_j and value Vhat_j;
+//     same registers are stored to LDS as bf16 tiles (Kbar as high and low
+//     parts in the K layout, Vhat in the V layout), and the token-to-block
+//     tile scale * Q_i KC^T (MFMA, high plus low part) gives the logits of
+//     the unselected columns, which enter the group's online softmax with
+//     weight n_j and value Vhat_j;
 // Exact and approximate terms share one running max, denominator and
 // accumulator; the order in which they enter is immaterial to the result.
 //
@@ -76,7 +77,14 @@ struct Cfg {
   static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
   static constexpr int BITS = 4 * TILE;                      // 2 x kMaxBlocks bits
   static constexpr int QBAR = BITS + 2 * (kMaxBlocks / 8);  // 2 x D floats
-  static constexpr int SMEM_FUSED = QBAR + 2 * D * 4;
+  // Low bf16 parts of the staged pooled keys (the token-to-block tile runs on
+  // Kbar = high + low): the unused second half of each K tile when a tile
+  // holds two sub-chunks' rows, else a region of their own.
+  static constexpr bool LO_IN_K = BLK >= 2 * SUB;
+  static constexpr int LOX = QBAR + 2 * D * 4;
+  static constexpr int KLO0 = LO_IN_K ? K0 + SUB * ROW : LOX;
+  static constexpr int KLO1 = LO_IN_K ? K1 + SUB * ROW : LOX + SUB * ROW;
+  static constexpr int SMEM_FUSED = LO_IN_K ? LOX : LOX + 2 * SUB * ROW;
   static constexpr int SMEM_DENSE = 4 * TILE;
   static_assert(DMA * WAVES * 1024 == TILE, "tile must split into whole 1 KB loads");
 };
@@ -255,6 +263,22 @@ __device__ __forceinline__ f32x16 score_tile(const char* ktile, const LaneOffset
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    const bf16x8 ka =
+        *reinterpret_cast<const bf16x8*>(ktile + 32 * mt * C::ROW + off.k[ks]);
+    acc = mfma32x32x16(ka, qreg[ks], acc);
+  }
+  return acc;
+}
+
+// acc + the S^T tile mt of a second K-layout tile (the low parts of the
+// staged pooled keys).
+template <int D, int BLK>
+__device__ __forceinline__ f32x16 score_tile_add(const char* ktile,
+                                                 const LaneOffsets<D, BLK>& off,
+                                                 const bf16x8* qreg, int mt, f32x16 acc) {
+  using C = Cfg<D, BLK>;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     const bf16x8 ka =
@@ -569,7 +593,9 @@ struct PooledStage {
       }
     }
   }
-  __device__ __forceinline__ void store(char* kt, char* vt, int tid) const {
+  // Kbar as bf16 high part (kt) and low part x - high (klo), both in the K
+  // layout; Vhat as bf16 in the V layout.
+  __device__ __forceinline__ void store(char* kt, char* klo, char* vt, int tid) const {
     const int row = tid / TPR, q = tid % TPR;
 #pragma unroll
     for (int c = 0; c < F4; ++c) {
@@ -584,8 +610,12 @@ struct PooledStage {
                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[3]) << 16);
         return r;
       };
-      *reinterpret_cast<u32x2*>(kt + row * C::ROW + ((d / 8) ^ swz_k<C::SEGS>(row)) * 16 + byte) =
-          pack4(k[c]);
+      f32x4 low;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) low[e] = k[c][e] - (float)(bf16)k[c][e];
+      const int koff = row * C::ROW + ((d / 8) ^ swz_k<C::SEGS>(row)) * 16 + byte;
+      *reinterpret_cast<u32x2*>(kt + koff) = pack4(k[c]);
+      *reinterpret_cast<u32x2*>(klo + koff) = pack4(low);
       *reinterpret_cast<u32x2*>(vt + row * C::ROW + ((d / 8) ^ swz_v<C::SEGS>(row)) * 16 + byte) =
           pack4(v[c]);
     }
@@ -594,18 +624,21 @@ struct PooledStage {
 
 // Zeroth-order terms (Eqs. 9-10) of staged rows 32 half .. 32 half + 31
 // whose bit is set in unsel, for this wave's 32 queries: logits
-// scale * q_r . Kbar_j from the token-to-block tile (Eq. 11; MFMA on bf16
-// Kbar), denominator weight n_j, numerator Vhat_j.  jb = pooled key of the
+// scale * q_r . Kbar_j from the token-to-block tile (Eq. 11; MFMA on Kbar
+// split into bf16 high and low parts, so that the logits keep about 16
+// significant bits: a single bf16 Kbar would move a logit of size |a| by
+// about |a| 2^-9, which matters where large approximate logits dominate a
+// row), denominator weight n_j, numerator Vhat_j.  jb = pooled key of the
 // first of those rows.
 template <int D, int BLK>
-__device__ __forceinline__ void approx_sub(const char* kt, const char* vt,
+__device__ __forceinline__ void approx_sub(const char* kt, const char* klo, const char* vt,
                                            const LaneOffsets<D, BLK>& off, const bf16x8* qreg,
                                            int half, uint32_t unsel, uint32_t jb, uint32_t N,
                                            int n_last, float c, float& m_run, float& l_run,
                                            f32x16* o, int lane) {
   using C = Cfg<D, BLK>;
   const int h = lane / 32;
-  f32x16 t = score_tile<D, BLK>(kt, off, qreg, half);
+  f32x16 t = score_tile_add<D, BLK>(klo, off, qreg, half, score_tile<D, BLK>(kt, off, qreg, half));
   // register r of this lane holds staged row 4 h + kRow[r]; with the lane's
   // bits pre-shifted, every test below is against a compile-time position
   const uint32_t uh = unsel >> (4 * h);
@@ -671,9 +704,10 @@ __device__ __forceinline__ void route_approx_phase(
   int buf = 0;
   for (uint32_t sb = 0; sb < nsub; ++sb) {
     char* kt = smem + (buf ? C::K1 : C::K0);
+    char* klo = smem + (buf ? C::KLO1 : C::KLO0);
     char* vt = smem + (buf ? C::V1 : C::V0);
     if (route) st.route(bits0, bits1, qbar_s, tau0, tau1, scale, sb * C::SUB, N, tid, lane, wave);
-    st.store(kt, vt, tid);
+    st.store(kt, klo, vt, tid);
     if (sb + 1 < nsub) st.load(kbar_h, vhat_h, (sb + 1) * C::SUB, N, tid);
     __syncthreads();  // staged rows and their bits visible; the other buffer's readers are done
     if (approx && grp_on) {
@@ -686,8 +720,8 @@ __device__ __forceinline__ void route_approx_phase(
       for (int half = 0; half < 2; ++half) {
         const uint32_t u = (uint32_t)(unsel >> (32 * half));
         if (u)
-          approx_sub<D, BLK>(kt, vt - C::V0, off, qreg, half, u, sb * C::SUB + 32 * half, N,
-                             n_last, c, m_run, l_run, o, lane);
+          approx_sub<D, BLK>(kt, klo, vt - C::V0, off, qreg, half, u, sb * C::SUB + 32 * half,
+                             N, n_last, c, m_run, l_run, o, lane);
       }
     }
     buf ^= 1;

@@ -12,10 +12,13 @@
 //   C_j = sum over block j's valid tokens t of (k_t - Kbar_j) v_t^T   (d x d).
 //
 // Two kernels:
-//   * kv_moments_kernel: C_j of every block, one MFMA product per block over
-//     its tokens, stored bf16 with the value dimension as rows
-//     (kvc[j][b][a] = C_j[a][b]), so that a 16-byte row segment is an MFMA
-//     operand fragment;
+//   * kv_moments_kernel: C_j = K_j^T V_j - Kbar_j Vhat_j^T of every block
+//     (the same sum, since Vhat_j is the sum of the block's values): the
+//     products of the exact bf16 keys and values accumulate in float32 on
+//     MFMA and the pooled outer product is subtracted in float32, so the only
+//     rounding of note is the final bf16 store, with the value dimension as
+//     rows (kvc[j][b][a] = C_j[a][b]) so that a 16-byte row segment is an
+//     MFMA operand fragment;
 //   * fo_kernel: after the fused forward has written O in float32, the row's
 //     log2 denominator lse2_r (in logit units, 2^lse2_r = sum of the row's
 //     2^(c s) weights) and the selection bitmaps, every row gains
@@ -58,19 +61,20 @@ struct KvCfg {
   static_assert((TP * 2) % 16 == 0, "operand rows must stay 16-byte aligned");
 };
 
-// One workgroup per block j of one head.  The block's centred keys and its
-// values are written transposed to LDS (dimension rows, token columns, zero
-// past the n_j valid tokens), so an MFMA fragment of eight consecutive
-// tokens is one 16-byte read; then
-//   out^T[a][b] = sum_t (k_t[a] - Kbar_j[a]) v_t[b]
-// tile by tile, A = centred-key rows, B = value rows.  The centred keys are
-// rounded to bf16 (the products accumulate in float32).
+// One workgroup per block j of one head.  The block's keys and values are
+// written transposed to LDS (dimension rows, token columns, zero past the n_j
+// valid tokens), so an MFMA fragment of eight consecutive tokens is one
+// 16-byte read; then, tile by tile,
+//   out^T[a][b] = sum_t k_t[a] v_t[b] - Kbar_j[a] Vhat_j[b]
+// with A = key rows, B = value rows.  Centring the keys before the product
+// would round each k_t - Kbar_j to bf16; this form multiplies exact bf16
+// inputs and cancels the mean in float32 instead.
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, const uint16_t* v,
-                                                         const float* kbar, uint16_t* kvc,
-                                                         int64_t L, uint32_t N) {
+                                                         const float* kbar, const float* vhat,
+                                                         uint16_t* kvc, int64_t L, uint32_t N) {
   using C = KvCfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) uint16_t kc_t[D][C::TP];
+  __shared__ __attribute__((aligned(16))) uint16_t k_t[D][C::TP];
   __shared__ __attribute__((aligned(16))) uint16_t v_t[D][C::TP];
   const uint32_t item = blockIdx.x;  // bh * N + j
   const uint32_t j = item % N;
@@ -79,30 +83,25 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
   const int n = (int)(rem < BLK ? rem : BLK);
   const uint16_t* kb = k + ((size_t)bh * L + (size_t)j * BLK) * D;
   const uint16_t* vb = v + ((size_t)bh * L + (size_t)j * BLK) * D;
-  const float* km = kbar + (size_t)item * D;
   const int tid = threadIdx.x;
 
   for (int e = tid; e < BLK * C::SEGS; e += C::NT) {
     const int t = e / C::SEGS, sg = e % C::SEGS;
     u32x4 kw = {0u, 0u, 0u, 0u}, vw = {0u, 0u, 0u, 0u};
-    f32x4 m0 = {0.f, 0.f, 0.f, 0.f}, m1 = {0.f, 0.f, 0.f, 0.f};
     if (t < n) {
       kw = *reinterpret_cast<const u32x4*>(kb + (size_t)t * D + 8 * sg);
       vw = *reinterpret_cast<const u32x4*>(vb + (size_t)t * D + 8 * sg);
-      m0 = *reinterpret_cast<const f32x4*>(km + 8 * sg);
-      m1 = *reinterpret_cast<const f32x4*>(km + 8 * sg + 4);
     }
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
-      const uint32_t kbits = (kw[e8 / 2] >> (16 * (e8 % 2))) & 0xffffu;
-      const float mean = e8 < 4 ? m0[e8] : m1[e8 - 4];
-      const bf16 centred = (bf16)(t < n ? bf16_bits_to_f32(kbits) - mean : 0.f);
-      kc_t[8 * sg + e8][t] = __builtin_bit_cast(uint16_t, centred);
+      k_t[8 * sg + e8][t] = (uint16_t)((kw[e8 / 2] >> (16 * (e8 % 2))) & 0xffffu);
       v_t[8 * sg + e8][t] = (uint16_t)((vw[e8 / 2] >> (16 * (e8 % 2))) & 0xffffu);
     }
   }
   __syncthreads();
 
+  const float* km = kbar + (size_t)item * D;
+  const float* vs = vhat + (size_t)item * D;
   const int wave = tid / kWave, lane = tid % kWave;
   const int h = lane / 32, l32 = lane % 32;
   for (int tile = wave; tile < C::TD * C::TD; tile += C::WAVES) {
@@ -112,20 +111,25 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kc_t[32 * ta + l32][16 * ks + 8 * h]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_t[32 * ta + l32][16 * ks + 8 * h]);
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(&v_t[32 * tb + l32][16 * ks + 8 * h]);
       acc = mfma32x32x16(a, b, acc);
     }
     // lane: value dim b = 32 tb + l32; key dims a = 32 ta + mfma_row(r, h),
     // four consecutive per group of four registers
+    const float vb_sum = vs[32 * tb + l32];
     uint16_t* orow = kvc + ((size_t)item * D + 32 * tb + l32) * D + 32 * ta;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 m = *reinterpret_cast<const f32x4*>(km + 32 * ta + 8 * r4 + 4 * h);
+      bf16 c[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] = (bf16)__builtin_fmaf(-m[e], vb_sum, acc[4 * r4 + e]);
       uint2 st;
-      st.x = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * r4 + 0]) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * r4 + 1]) << 16);
-      st.y = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * r4 + 2]) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * r4 + 3]) << 16);
+      st.x = (uint32_t)__builtin_bit_cast(uint16_t, c[0]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, c[1]) << 16);
+      st.y = (uint32_t)__builtin_bit_cast(uint16_t, c[2]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, c[3]) << 16);
       *reinterpret_cast<uint2*>(orow + 8 * r4 + 4 * h) = st;
     }
   }
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(512) void fo_kernel(FoArgs a) {
 }  // namespace
 
 hipError_t launch_kv_moments(const Shape& s, const void* k, const void* v, const float* kbar,
-                             void* kvc, hipStream_t stream) {
+                             const float* vhat, void* kvc, hipStream_t stream) {
   const dim3 grid((uint32_t)(s.bh * s.N));
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
@@ -373,7 +377,7 @@ hipError_t launch_kv_moments(const Shape& s, const void* k, const void* v, const
 #define SOLATTN_KV(DD, BB)                                                                  \
   if (s.d == DD && s.block == BB) {                                                         \
     hipLaunchKernelGGL((kv_moments_kernel<DD, BB>), grid, dim3(256), 0, stream, kk, vv, kbar, \
-                       out, s.L, N);                                                        \
+                       vhat, out, s.L, N);                                                  \
     return hipGetLastError();                                                               \
   }
   SOLATTN_KV(128, 128)

@@ -38,9 +38,10 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
                       float* out_f32, float* lse2, hipStream_t stream);
 
 // First-order term of the unselected blocks.
-// kvc[bh][j][b][a] = sum over block j's valid tokens t of v_t[b] (k_t[a] - Kbar_j[a]), bf16.
+// kvc[bh][j][b][a] = sum over block j's valid tokens t of v_t[b] (k_t[a] - Kbar_j[a]), bf16,
+// formed as K_j^T V_j - Kbar_j Vhat_j^T.
 hipError_t launch_kv_moments(const Shape& s, const void* k, const void* v, const float* kbar,
-                             void* kvc, hipStream_t stream);
+                             const float* vhat, void* kvc, hipStream_t stream);
 // out = bf16(o32 + sum over j unselected (sel_mask) of 2^(c q.Kbar_j - lse2) scale C_j^T q)
 // row by row; o32, lse2 and sel_mask as written by launch_fwd.
 hipError_t launch_first_order(const Shape& s, const void* q, const float* kbar, const void* kvc,

@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/solattn.h"
+#include "solattn.h"
 #include "launch.hpp"
 
 namespace {
@@ -141,14 +141,15 @@ int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k,
 }
 
 int solattn_kv_moments(const solattn_problem_t* p, const void* k, const void* v,
-                       const float* kbar, void* kvc, void* stream) {
+                       const float* kbar, const float* vhat, void* kvc, void* stream) {
   solattn::Shape s;
   bool empty = false;
   int rc = check_shape(p, &s, &empty);
   if (rc != SOLATTN_OK) return rc;
   if (empty) return SOLATTN_OK;
-  if (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(kbar) || !ok_ptr(kvc)) return SOLATTN_E_INVALID_ARG;
-  return from_hip(solattn::launch_kv_moments(s, k, v, kbar, kvc,
+  if (!ok_ptr(k) || !ok_ptr(v) || !ok_ptr(kbar) || !ok_ptr(vhat) || !ok_ptr(kvc))
+    return SOLATTN_E_INVALID_ARG;
+  return from_hip(solattn::launch_kv_moments(s, k, v, kbar, vhat, kvc,
                                              static_cast<hipStream_t>(stream)));
 }
 

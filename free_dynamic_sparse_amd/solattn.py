@@ -62,7 +62,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.solattn_proxy_map.argtypes = [pp, vp, vp, vp, vp]
     lib.solattn_select_topk.argtypes = [pp, vp, ctypes.c_int64, vp, vp, vp]
     lib.solattn_select_topp.argtypes = [pp, vp, ctypes.c_float, vp, vp, vp]
-    lib.solattn_kv_moments.argtypes = [pp, vp, vp, vp, vp, vp]
+    lib.solattn_kv_moments.argtypes = [pp, vp, vp, vp, vp, vp, vp]
     lib.solattn_fwd_first_order_workspace.argtypes = [pp]
     lib.solattn_fwd_first_order_workspace.restype = ctypes.c_size_t
     lib.solattn_fwd_first_order.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -181,14 +181,15 @@ def solattn_fwd_masked(p: Problem, q, k, v, kbar, vhat, sel_in, out, stream=None
            "solattn_fwd_masked")
 
 
-def solattn_kv_moments(p: Problem, k, v, kbar, kvc, stream=None) -> None:
+def solattn_kv_moments(p: Problem, k, v, kbar, vhat, kvc, stream=None) -> None:
     full, pooled, N = _dims(p)
     _need(k, torch.bfloat16, full, "k")
     _need(v, torch.bfloat16, full, "v")
     _need(kbar, torch.float32, pooled, "kbar")
+    _need(vhat, torch.float32, pooled, "vhat")
     _need(kvc, torch.bfloat16, (p.batch, p.heads, N, p.head_dim, p.head_dim), "kvc")
-    _check(LIB.solattn_kv_moments(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(kbar), _ptr(kvc),
-                                  _stream(stream)), "solattn_kv_moments")
+    _check(LIB.solattn_kv_moments(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(kbar), _ptr(vhat),
+                                  _ptr(kvc), _stream(stream)), "solattn_kv_moments")
 
 
 def solattn_fwd_first_order_workspace(p: Problem) -> int:
@@ -319,7 +320,7 @@ def forward_first_order(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta:
         out = torch.empty_like(q)
     solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, stream)
     solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma, stream)
-    solattn_kv_moments(p, k, v, ws.kbar, fws.kvc, stream)
+    solattn_kv_moments(p, k, v, ws.kbar, ws.vhat, fws.kvc, stream)
     solattn_fwd_first_order(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, fws.kvc, ws.tau, out,
                             fws.scratch, stream)
     return out

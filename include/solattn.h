@@ -171,12 +171,14 @@ int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k,
  *   C_j = sum over block j's valid tokens t of (k_t - Kbar_j) v_t^T  (d x d).
  *
  * solattn_kv_moments: C_j of every block.
- *   k, v  in:  bf16 [B, H, L, d]
- *   kbar  in:  f32 [B, H, N, d]  from solattn_pool
- *   kvc   out: bf16 [B, H, N, d, d], value dimension first:
- *              element [b][h][j][e][a] is C_j[a][e] (key dim a, value dim e)
- * The centred keys k_t - Kbar_j are rounded to bf16 and the products
- * accumulate in float32.  beta, chunk and flags are ignored.
+ *   k, v        in:  bf16 [B, H, L, d]
+ *   kbar, vhat  in:  f32 [B, H, N, d]  from solattn_pool
+ *   kvc         out: bf16 [B, H, N, d, d], value dimension first:
+ *                    element [b][h][j][e][a] is C_j[a][e] (key dim a, value dim e)
+ * Formed as K_j^T V_j - Kbar_j Vhat_j^T: products of the bf16 inputs
+ * accumulate in float32, the pooled outer product is subtracted in float32
+ * and the result is rounded to bf16 once.  beta, chunk and flags are
+ * ignored.
  *
  * solattn_fwd_first_order: solattn_fwd (threshold routing, exact selected
  * blocks, zeroth-order unselected blocks) with the first-order term of every
@@ -203,7 +205,7 @@ int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k,
  * empty or invalid problem.
  */
 int solattn_kv_moments(const solattn_problem_t* p, const void* k, const void* v,
-                       const float* kbar, void* kvc, void* stream);
+                       const float* kbar, const float* vhat, void* kvc, void* stream);
 size_t solattn_fwd_first_order_workspace(const solattn_problem_t* p);
 int solattn_fwd_first_order(const solattn_problem_t* p, const void* q, const void* k,
                             const void* v, const float* qbar, const float* kbar,

@@ -219,13 +219,13 @@ def test_first_order_entry_points_reject_bad_arguments(sa):
     assert fo(sa.problem(1, 2, 4096, 96, 128, 32, 1.0), ok) == -2
     empty = sa.problem(1, 0, 4096, 128, 128, 32, 1.0)
     assert fo(empty, [None] * 10, 0) == 0
-    # kv moments: k, v, kbar, kvc
-    for i in range(4):
-        ptrs = [P(FAKE)] * 4
+    # kv moments: k, v, kbar, vhat, kvc
+    for i in range(5):
+        ptrs = [P(FAKE)] * 5
         ptrs[i] = None
         assert lib.solattn_kv_moments(ctypes.byref(p), *ptrs, None) == -1
         ptrs[i] = P(FAKE + 8)
         assert lib.solattn_kv_moments(ctypes.byref(p), *ptrs, None) == -1
-    assert lib.solattn_kv_moments(ctypes.byref(empty), None, None, None, None, None) == 0
+    assert lib.solattn_kv_moments(ctypes.byref(empty), *[None] * 5, None) == 0
     assert lib.solattn_kv_moments(ctypes.byref(sa.problem(1, 1, 64, 128, 32)),
-                                  *[P(FAKE)] * 4, None) == -2
+                                  *[P(FAKE)] * 5, None) == -2

@@ -2,13 +2,13 @@
 solattn_fwd_first_order, through the C ABI) against the oracle.
 
 Tolerances.
-  * Block moments C_j: the centred keys k_t - Kbar_j are rounded to bf16
-    (unit roundoff u = 2^-8) and the products accumulate in float32, then the
-    result is rounded to bf16; Kbar_j itself is the float32 pooled mean.  So
-    each element is within
-        u |C_j[a][b]| + 2 u A[a][b] + dK[a] sum_t |v_t[b]|,
-    A[a][b] = sum_t |k_t[a] - Kbar_j[a]| |v_t[b]|, dK = the pooled mean's
-    float32 bound 2^-24 (n + 2) mean_t |k_t[a]|.
+  * Block moments C_j = K_j^T V_j - Kbar_j Vhat_j^T: exact bf16 products
+    accumulated in float32 (error <= 2^-24 (n + 2) S[a][b] with
+    S[a][b] = sum_t |k_t[a]| |v_t[b]|), the float32 pooled Kbar_j and Vhat_j
+    (each within 2^-24 (n + 2) of the sums of absolute values they come
+    from), one float32 product and subtraction, then one bf16 rounding (unit
+    roundoff u = 2^-8).  So each element is within
+        u |C_j[a][b]| + 2^-24 (3 n + 8) (S[a][b] + mean_t |k_t[a]| sum_t |v_t[b]|).
   * Outputs: the bf16 output bounds of the zeroth-order path (max-abs 2e-2,
     mean-relative 5e-3), after checking the selection as for solattn_fwd
     (in-band flips only; the oracle then takes the GPU's selection).
@@ -72,7 +72,7 @@ def run_both(sa, q, k, v, beta, block, chunk=16, want_kvc=False):
     sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma)
     sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out0, ws.sel_mask,
                    ws.sel_count)
-    sa.solattn_kv_moments(p, k, v, ws.kbar, fws.kvc)
+    sa.solattn_kv_moments(p, k, v, ws.kbar, ws.vhat, fws.kvc)
     sa.solattn_fwd_first_order(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, fws.kvc, ws.tau, out1,
                                fws.scratch)
     torch.cuda.synchronize()
@@ -93,21 +93,23 @@ def check_kvc(kvc_gpu, k, v, block, tag):
     worst = 0.0
     for j in range(ref.num_blocks(L, block)):
         a, b = ref.block_range(L, block, j)
-        kj = k[a:b].astype(np.float64)
+        n = b - a
+        kj = np.abs(k[a:b].astype(np.float64))
         vj = np.abs(v[a:b].astype(np.float64))
-        dk = np.abs(kj - kj.mean(axis=0))
-        A = dk.T @ vj
-        kbar_err = 2.0 ** -24 * (b - a + 2) * np.abs(kj).mean(axis=0)
-        tol = u * np.abs(want[j]) + 2 * u * A + kbar_err[:, None] * vj.sum(axis=0)[None, :] + 1e-30
+        S = kj.T @ vj
+        pooled = kj.mean(axis=0)[:, None] * vj.sum(axis=0)[None, :]
+        tol = u * np.abs(want[j]) + 2.0 ** -24 * (3 * n + 8) * (S + pooled) + 1e-30
         err = np.abs(kvc_gpu[j].T - want[j])
         assert np.all(err <= tol), f"{tag}: block {j}, max excess {(err - tol).max():.3g}"
         worst = max(worst, float((err / tol).max()))
     return worst
 
 
-def check_first_order(g, q, k, v, beta, block, rows=None, tag=""):
+def check_first_order(g, q, k, v, beta, block, rows=None, tag="", scaled_abs=False):
     """One head: selection as for solattn_fwd, then the first-order output
-    against the oracle with the GPU's selection."""
+    against the oracle with the GPU's selection.  scaled_abs: the max-abs bar
+    applies to |err| / max(1, |ref|) (for outputs far outside the unit range,
+    where bf16 rounding alone exceeds the absolute bar)."""
     L = q.shape[0]
     r = ref.solattn_head(q, k, v, beta, block, rows=[])
     st = parity.selection_check(g["sel"], r)
@@ -121,13 +123,20 @@ def check_first_order(g, q, k, v, beta, block, rows=None, tag=""):
         want1[a:b] = ref.forward_block(q, k, v, r.kbar, r.vhat, sel[i], i, block, r.scale,
                                        first_order=True)
         want0[a:b] = ref.forward_block(q, k, v, r.kbar, r.vhat, sel[i], i, block, r.scale)
-    max_abs, mean_rel, finite = parity.output_errors(g["out1"], want1)
     ok = np.isfinite(want1)
+    if scaled_abs:
+        scale_ref = np.maximum(1.0, np.abs(np.where(ok, want1, 0.0)))
+        max_abs, mean_rel, finite = parity.output_errors(g["out1"] / scale_ref, want1 / scale_ref)
+        mean_rel = parity.output_errors(g["out1"], want1)[1]
+    else:
+        max_abs, mean_rel, finite = parity.output_errors(g["out1"], want1)
     change = float(np.abs(want1[ok] - want0[ok]).mean())
     size = float(np.abs(want1[ok]).mean())
     err1 = float(np.abs(g["out1"][ok] - want1[ok]).mean())
+    mean_rel0 = parity.output_errors(g["out0"], want0)[1]
     rep = dict(tag=tag, density=float(sel.mean()), flips=st.in_band, max_abs=max_abs,
-               mean_rel=mean_rel, change_rel=change / size, err_over_change=err1 / max(change, 1e-30))
+               mean_rel=mean_rel, mean_rel_zeroth=mean_rel0, change_rel=change / size,
+               err_over_change=err1 / max(change, 1e-30))
     log(f"  {rep}")
     assert finite, f"{tag}: non-finite output"
     assert max_abs <= parity.MAX_ABS, f"{tag}: max-abs {max_abs}"
@@ -173,6 +182,25 @@ def test_ragged_shapes(sa, d, block, L, beta):
     check_workload(sa, w, beta)
 
 
+@pytest.mark.parametrize("d,block,L,grid", [(64, 64, 1000, (1, 1, 1000)),
+                                            (128, 128, 4096, (1, 64, 64))])
+def test_peaked_heads_at_beta_plus_inf(sa, d, block, L, grid):
+    # Peaked positional heads with every block approximated: the first-order
+    # term dominates (outputs reach about 30, several times the dense
+    # output's norm away from it) and the kernel must still follow the oracle.
+    w = synth.Workload("peaked_fo", B=1, H=2, L=L, d=d, block=block, chunk=16, seed=4,
+                       kind="pos", grid=grid, alpha=4.0)
+    q, k, v = synth.make_inputs(w)
+    g = run_both(sa, q, k, v, math.inf, block, want_kvc=True)
+    for h in range(w.H):
+        check_kvc(g["kvc"][0, h], k[0, h], v[0, h], block, f"peaked h{h}")
+        gh = {key: val[0, h] for key, val in g.items() if key != "kvc"}
+        rep = check_first_order(gh, q[0, h], k[0, h], v[0, h], math.inf, block,
+                                tag=f"peaked d{d} h{h}", scaled_abs=True)
+        assert rep["change_rel"] > 0.5
+        assert rep["mean_rel_zeroth"] <= parity.MEAN_REL
+
+
 def test_beta_minus_inf_leaves_the_output_unchanged(sa):
     # nothing is unselected: the first-order forward is the zeroth-order one
     w = synth.WORKLOADS["tiny"]
@@ -183,8 +211,10 @@ def test_beta_minus_inf_leaves_the_output_unchanged(sa):
 
 
 def test_block_constant_keys_give_zero_moments(sa):
-    # keys constant within each block: C_j = 0 exactly and the output is the
-    # zeroth-order one
+    # keys constant within each block: C_j = 0 (the two float32 sums of
+    # K_j^T V_j - Kbar_j Vhat_j^T cancel up to their rounding), so the
+    # correction is below 2^-20 of the output's scale: each bf16 output moves
+    # by at most one unit in its last place or by that absolute amount
     rng = np.random.default_rng(12)
     B, H, L, d, block = 1, 2, 1000, 128, 128
     N = ref.num_blocks(L, block)
@@ -193,8 +223,10 @@ def test_block_constant_keys_give_zero_moments(sa):
     q = synth.round_bf16(rng.standard_normal((B, H, L, d)).astype(np.float32))
     v = synth.round_bf16(rng.standard_normal((B, H, L, d)).astype(np.float32))
     g = run_both(sa, q, k, v, 1.0, block, want_kvc=True)
-    assert np.all(g["kvc"] == 0.0)
-    np.testing.assert_array_equal(g["out1"], g["out0"])
+    for h in range(H):
+        check_kvc(g["kvc"][0, h], k[0, h], v[0, h], block, f"constant keys h{h}")
+    np.testing.assert_allclose(g["out1"], g["out0"], rtol=2.0 ** -7,
+                               atol=2.0 ** -20 * float(np.abs(g["out0"]).max()))
 
 
 def test_repeat_calls_are_bitwise_identical(sa):

@@ -170,6 +170,17 @@ def test_beta_plus_inf_is_all_approximation(sa):
     assert not g["sel"].any()
 
 
+@pytest.mark.parametrize("d,block,L,grid", [(64, 64, 1000, (1, 1, 1000)),
+                                            (128, 128, 4096, (1, 64, 64))])
+def test_peaked_heads_all_approximated(sa, d, block, L, grid):
+    # Peaked positional heads (alpha = 4) at beta = +inf: every block is
+    # approximated and the logits run to a few hundred, so the approximation
+    # logits must keep more precision than a bf16 Kbar gives.
+    w = synth.Workload("peaked", B=1, H=2, L=L, d=d, block=block, chunk=16, seed=4,
+                       kind="pos", grid=grid, alpha=4.0)
+    check_all_heads(sa, w, math.inf)
+
+
 @pytest.mark.parametrize("beta", [0.5, 2.0])
 def test_exact_only_mode(sa, beta):
     log(f"exact-only beta={beta}")

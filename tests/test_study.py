@@ -50,6 +50,32 @@ def test_oracle_approximation_lowers_error(name, heads):
         assert e_full < e_exact, (name, h, beta, e_full, e_exact)
 
 
+def test_oracle_first_order_helps_flat_heads_and_diverges_on_peaked_ones():
+    # The first-order study's two regimes, on fixed seeded inputs (empirical,
+    # a regression check like the one above):
+    #   * i.i.d. (flat) attention at beta = 1: the first-order term moves the
+    #     output closer to dense attention;
+    #   * a peaked positional head with every block approximated: the linear
+    #     term of exp around the block's mean score turns large and negative
+    #     for keys far below the mean, and the output moves far away.
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = synth.make_head(w, 0, 0)
+    s = ref.default_scale(w.d)
+    dense = ref.dense(q, k, v, s)
+    r = ref.solattn_head(q, k, v, 1.0, w.block, rows=[])
+    zeroth = rel_l2(ref.forward(q, k, v, r.sel, w.block, s), dense)
+    first = rel_l2(ref.forward(q, k, v, r.sel, w.block, s, first_order=True), dense)
+    assert first < 0.8 * zeroth, (first, zeroth)
+
+    wp = synth.Workload("peaked", B=1, H=1, L=1000, d=64, block=64, chunk=16, seed=4,
+                        kind="pos", grid=(1, 1, 1000), alpha=4.0)
+    q, k, v = synth.make_head(wp, 0, 0)
+    dense = ref.dense(q, k, v, ref.default_scale(64))
+    zeroth = rel_l2(ref.solattn_head(q, k, v, math.inf, 64).out, dense)
+    first = rel_l2(ref.solattn_head(q, k, v, math.inf, 64, first_order=True).out, dense)
+    assert first > 2.0 * zeroth, (first, zeroth)
+
+
 @pytest.mark.gpu
 def test_gpu_study_matches_oracle():
     if not torch.cuda.is_available():
