@@ -30,9 +30,10 @@
 // fo_kernel layout.  One workgroup of 8 waves serves G consecutive query
 // blocks of one head (G = 2 for 128-token blocks, 4 for 64), one wave per 32
 // query rows.  It walks the union of the G blocks' unselected sets; each
-// C_j of the union is streamed into LDS once (direct-to-LDS loads, double
-// buffered, one workgroup barrier per block) and used by the groups that did
-// not select j.  MFMA layout as in the fused kernel, transposed so that each
+// C_j of the union is streamed into LDS once (direct-to-LDS loads, one
+// workgroup barrier per block) and used by the groups that did not select j,
+// with the loads running two blocks ahead (three buffers).
+// MFMA layout as in the fused kernel, transposed so that each
 // lane owns one query:
 //   T^T = C_j^T Q^T   A = rows of kvc_j from LDS, B = Q^T in registers;
 //   O^T += w_j T^T    w_j = the lane's own weight, a per-lane scalar.
@@ -106,6 +107,12 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
   const int h = lane / 32, l32 = lane % 32;
   for (int tile = wave; tile < C::TD * C::TD; tile += C::WAVES) {
     const int ta = tile / C::TD, tb = tile % C::TD;
+    // pooled values first (a later load would otherwise wait for the stores)
+    const float vb_sum = vs[32 * tb + l32];
+    f32x4 m[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      m[r4] = *reinterpret_cast<const f32x4*>(km + 32 * ta + 8 * r4 + 4 * h);
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -117,14 +124,13 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
     }
     // lane: value dim b = 32 tb + l32; key dims a = 32 ta + mfma_row(r, h),
     // four consecutive per group of four registers
-    const float vb_sum = vs[32 * tb + l32];
     uint16_t* orow = kvc + ((size_t)item * D + 32 * tb + l32) * D + 32 * ta;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 m = *reinterpret_cast<const f32x4*>(km + 32 * ta + 8 * r4 + 4 * h);
       bf16 c[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] = (bf16)__builtin_fmaf(-m[e], vb_sum, acc[4 * r4 + e]);
+      for (int e = 0; e < 4; ++e)
+        c[e] = (bf16)__builtin_fmaf(-m[r4][e], vb_sum, acc[4 * r4 + e]);
       uint2 st;
       st.x = (uint32_t)__builtin_bit_cast(uint16_t, c[0]) |
              ((uint32_t)__builtin_bit_cast(uint16_t, c[1]) << 16);
@@ -136,6 +142,11 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
 }
 
 // ------------------------------------------------------------ correction
+
+// Largest N the correction kernel keeps per-block selection words for in LDS
+// (the entry point allows N <= 8192, the fused kernel's own limit).
+constexpr int kFoMaxBlocks = 8192;
+constexpr int kFoMaxGroups = kFoMaxBlocks / 32;
 
 template <int D, int BLK>
 struct FoCfg {
@@ -152,8 +163,12 @@ struct FoCfg {
   static constexpr int ROWS_1K = 1024 / ROW;
   static constexpr int KB = 32 * ROW;          // 32 staged pooled keys, bf16
   static constexpr int WT = 32 * 32 * 4;       // one wave's weight table (32 keys x 32 rows)
-  static constexpr int C0 = 0, C1 = CT, KHI = 2 * CT, KLO = KHI + KB, WTAB = KLO + KB;
-  static constexpr int SMEM = WTAB + WAVES * WT;
+  static constexpr int NBUF = 3;               // C_j buffers: loads run two blocks ahead
+  static constexpr int C0 = 0, KHI = NBUF * CT, KLO = KHI + KB, WTAB = KLO + KB;
+  // unselected words, u32 [1 + G][kFoMaxGroups]: the union of the G blocks',
+  // then each block's own
+  static constexpr int SELW = WTAB + WAVES * WT;
+  static constexpr int SMEM = SELW + (1 + G) * kFoMaxGroups * 4;
   static_assert(DMA >= 1 && DMA * WAVES * 1024 == CT, "a C_j tile splits into whole 1 KB loads");
 };
 
@@ -230,11 +245,23 @@ __global__ __launch_bounds__(512) void fo_kernel(FoArgs a) {
     const uint32_t valid = rem >= 32u ? ~0u : ((1u << rem) - 1u);
     return ~s & valid;
   };
-  auto union_word = [&](uint32_t gb) -> uint32_t {
+  // The tuple's unselected words go to LDS once, so that walking them later
+  // issues no vector-memory load (whose wait would also wait for the C_j
+  // loads in flight).
+  uint32_t* usel = reinterpret_cast<uint32_t*>(smem + C::SELW);
+  for (uint32_t gb = (uint32_t)tid; gb < ngb; gb += C::NT) {
     uint32_t u = 0u;
 #pragma unroll
-    for (int g = 0; g < C::G; ++g) u |= unsel_word(i0 + g, gb);
-    return __builtin_amdgcn_readfirstlane(u);
+    for (int g = 0; g < C::G; ++g) {
+      const uint32_t w = unsel_word(i0 + g, gb);
+      usel[(1 + g) * kFoMaxGroups + gb] = w;
+      u |= w;
+    }
+    usel[gb] = u;
+  }
+  __syncthreads();
+  auto union_word = [&](uint32_t gb) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(usel[gb]);
   };
   // Smallest j >= from unselected by any block of the tuple, or N.
   auto next_block = [&](uint32_t from) -> uint32_t {
@@ -263,7 +290,7 @@ __global__ __launch_bounds__(512) void fo_kernel(FoArgs a) {
   const uint16_t* kvc_h = a.kvc + (size_t)bh * N * D * D;
   auto issue = [&](uint32_t j, int buf) {
     const uint16_t* src = uniform_ptr(kvc_h + (size_t)j * D * D);
-    const uint32_t dst = lbase + (uint32_t)(buf ? C::C1 : C::C0);
+    const uint32_t dst = lbase + (uint32_t)(C::C0 + buf * C::CT);
 #pragma unroll
     for (int c = 0; c < C::DMA; ++c)
       lds_dma_16b(doff[c], src, dst + (uint32_t)(wave + c * C::WAVES) * 1024u);
@@ -273,7 +300,9 @@ __global__ __launch_bounds__(512) void fo_kernel(FoArgs a) {
 
   settle_vm();
   uint32_t j = next_block(0);
+  uint32_t jn = j < N ? next_block(j + 1) : N;
   if (j < N) issue(j, 0);
+  if (jn < N) issue(jn, 1);
   int buf = 0;
   uint32_t staged = ~0u, own = 0u;
   while (j < N) {
@@ -300,7 +329,7 @@ __global__ __launch_bounds__(512) void fo_kernel(FoArgs a) {
         *reinterpret_cast<bf16x8*>(smem + C::KLO + off) = lo;
       }
       barrier_lds();
-      own = __builtin_amdgcn_readfirstlane(grp_on ? unsel_word(i_g, gb) : 0u);
+      own = __builtin_amdgcn_readfirstlane(grp_on ? usel[(1 + grp) * kFoMaxGroups + gb] : 0u);
       if (own) {
         // logits of the 32 staged keys for this wave's 32 queries:
         // lane = query l32, register r = key mfma_row(r, h)
@@ -322,12 +351,18 @@ __global__ __launch_bounds__(512) void fo_kernel(FoArgs a) {
       }
       staged = gb;
     }
-    const uint32_t jn = next_block(j + 1);
-    wait_vm<0>();
-    barrier_lds();  // C_j is in buffer buf; everyone is done with the other buffer
-    if (jn < N) issue(jn, buf ^ 1);
+    const uint32_t jnn = jn < N ? next_block(jn + 1) : N;
+    // C_j (buffer buf) has landed once at most the next block's loads are
+    // outstanding; after the barrier everyone is done with block j - 1's
+    // buffer, which takes the block after next.
+    if (jn < N)
+      wait_vm<C::DMA>();
+    else
+      wait_vm<0>();
+    barrier_lds();
+    if (jnn < N) issue(jnn, buf == 0 ? C::NBUF - 1 : buf - 1);
     if ((own >> (j % 32)) & 1u) {
-      const char* ct = smem + (buf ? C::C1 : C::C0);
+      const char* ct = smem + C::C0 + buf * C::CT;
       const float w = wtab[(j % 32) * 32 + l32];
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
@@ -342,19 +377,28 @@ __global__ __launch_bounds__(512) void fo_kernel(FoArgs a) {
         for (int r = 0; r < 16; ++r) o[dt][r] = __builtin_fmaf(w, t[r], o[dt][r]);
       }
     }
-    buf ^= 1;
+    buf = buf + 1 == C::NBUF ? 0 : buf + 1;
     j = jn;
+    jn = jnn;
   }
 
   if (row_on) {
+    // all loads first: the stores to out could alias o32 as far as the
+    // compiler knows, which would otherwise serialise every load
     const float* src = a.o32 + head + row_g * D;
     uint16_t* dst = a.out + head + row_g * D;
+    f32x4 xs[C::DT][4];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        xs[dt][r4] = *reinterpret_cast<const f32x4*>(src + 32 * dt + 8 * r4 + 4 * h);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * dt + 8 * r4 + 4 * h;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + d0);
+        const f32x4 x = xs[dt][r4];
         uint2 st;
         st.x = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)(x[0] + o[dt][4 * r4 + 0])) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)(x[1] + o[dt][4 * r4 + 1])) << 16);
@@ -391,6 +435,7 @@ hipError_t launch_kv_moments(const Shape& s, const void* k, const void* v, const
 hipError_t launch_first_order(const Shape& s, const void* q, const float* kbar, const void* kvc,
                               const uint64_t* sel_mask, const float* lse2, const float* o32,
                               void* out, hipStream_t stream) {
+  if (s.N > kFoMaxBlocks) return hipErrorInvalidValue;
   FoArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kbar = kbar;
