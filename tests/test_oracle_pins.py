@@ -111,6 +111,20 @@ def test_mean_density_tracks_gaussian_tail_long_row():
     assert abs(r.sel.mean() - phi_sf(1.0)) <= 0.003
 
 
+def test_two_blocks_put_tau_on_the_larger_score():
+    # A proxy row of two entries a < b has mean (a + b) / 2 and population
+    # std (b - a) / 2, so at beta = 1 the threshold is exactly b: the larger
+    # block passes the >= test and the smaller does not.  Small integers keep
+    # every step exact in float64.
+    q = np.array([[1.0], [1.0]])
+    k = np.array([[1.0], [3.0]])
+    v = np.array([[1.0], [2.0]])
+    r = ref.solattn_head(q, k, v, 1.0, 1, scale=1.0)
+    assert np.all(r.shat == [[1.0, 3.0], [1.0, 3.0]])
+    assert np.all(r.tau == 3.0)
+    assert r.sel.tolist() == [[False, True], [False, True]]
+
+
 def test_selection_invariances():
     w, q, k, v = small(L=4096, d=64, block=64, kind="pos", grid=(1, 64, 64))
     base = ref.solattn_head(q, k, v, 1.0, 64, rows=[])
