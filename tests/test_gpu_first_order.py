@@ -201,6 +201,16 @@ def test_peaked_heads_at_beta_plus_inf(sa, d, block, L, grid):
         assert rep["mean_rel_zeroth"] <= parity.MEAN_REL
 
 
+@pytest.mark.parametrize("case", range(4))
+def test_random_shapes(sa, case):
+    # the first four of the seeded random problems of the zeroth-order tests
+    from tests.test_gpu_parity import RANDOM_SHAPES
+    B, H, L, d, block, chunk, beta, kind = RANDOM_SHAPES[case]
+    w = synth.Workload(f"random{case}", B=B, H=H, L=L, d=d, block=block, chunk=chunk,
+                       seed=100 + case, kind=kind, grid=(1, 1, L))
+    check_workload(sa, w, beta)
+
+
 def test_beta_minus_inf_leaves_the_output_unchanged(sa):
     # nothing is unselected: the first-order forward is the zeroth-order one
     w = synth.WORKLOADS["tiny"]

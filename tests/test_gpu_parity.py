@@ -181,6 +181,30 @@ def test_peaked_heads_all_approximated(sa, d, block, L, grid):
     check_all_heads(sa, w, math.inf)
 
 
+def random_shapes(n=12, seed=2026):
+    """Seeded random problems: batch, heads, ragged L, d, block, chunk, beta
+    and input kind, drawn once (the same list on every run)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 4500)),
+                    int(rng.choice([64, 128])), int(rng.choice([64, 128])),
+                    int(rng.integers(1, 65)), float(np.round(rng.uniform(-1.0, 3.0), 2)),
+                    str(rng.choice(["iid", "pos"]))))
+    return out
+
+
+RANDOM_SHAPES = random_shapes()
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_SHAPES)))
+def test_random_shapes(sa, case):
+    B, H, L, d, block, chunk, beta, kind = RANDOM_SHAPES[case]
+    w = synth.Workload(f"random{case}", B=B, H=H, L=L, d=d, block=block, chunk=chunk,
+                       seed=100 + case, kind=kind, grid=(1, 1, L))
+    check_all_heads(sa, w, beta)
+
+
 @pytest.mark.parametrize("beta", [0.5, 2.0])
 def test_exact_only_mode(sa, beta):
     log(f"exact-only beta={beta}")
