@@ -109,7 +109,9 @@ def cpu_baseline(w: synth.Workload, beta: float, heads: int = 3):
             "sample": f"heads 0-{heads - 1} of {w.H} at beta={beta}: pooling, moments, "
                       f"thresholds, selection and all {w.N} query blocks' outputs per head, "
                       f"float64 NumPy; {dt:.1f} s",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0)),
+            "extrapolated_seconds_all_heads": dt * w.H / heads,
+            "extrapolation": f"measured seconds x {w.H}/{heads} heads (an estimate, not measured)"}
 
 
 def _to_device(w: synth.Workload):
@@ -395,7 +397,7 @@ def routing_study(sa, w: synth.Workload, beta: float):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--block", type=int, default=0,
