@@ -55,17 +55,24 @@ template <int D, int BLK>
 struct KvCfg {
   static constexpr int NT = 256;
   static constexpr int WAVES = NT / kWave;
-  static constexpr int TP = BLK + 8;    // bf16 per row of the transposed token tiles
   static constexpr int KS = BLK / 16;   // k-steps over the tokens
   static constexpr int TD = D / 32;     // 32-wide tiles per dimension
   static constexpr int SEGS = D / 8;    // 16-byte segments in a bf16 row of K or V
-  static_assert((TP * 2) % 16 == 0, "operand rows must stay 16-byte aligned");
+  static constexpr int ROW = 2 * D;     // bytes per bf16 row
 };
 
+typedef short kv_v4i16 __attribute__((ext_vector_type(4)));
+
+// XOR swizzle of a row's 16-byte segments: rows r .. r + 3 land in disjoint
+// 64-byte bank ranges for the transposed reads below.
+__device__ __forceinline__ int kv_swz(int r, int segs) { return (4 * (r % 4)) % segs; }
+
 // One workgroup per block j of one head.  The block's keys and values are
-// written transposed to LDS (dimension rows, token columns, zero past the n_j
-// valid tokens), so an MFMA fragment of eight consecutive tokens is one
-// 16-byte read; then, tile by tile,
+// staged row-major in LDS (16-byte writes, zero past the n_j valid tokens)
+// and read back transposed (ds_read_b64_tr_b16): lane l gets dimension
+// 32 t + l % 32 and the eight tokens 16 kk + 4 (l / 32) + {0..3, 8..11} of
+// k-step kk, the same tokens for both operands, so each MFMA contracts over
+// the 16 tokens of its k-step.  Tile by tile,
 //   out^T[a][b] = sum_t k_t[a] v_t[b] - Kbar_j[a] Vhat_j[b]
 // with A = key rows, B = value rows.  Centring the keys before the product
 // would round each k_t - Kbar_j to bf16; this form multiplies exact bf16
@@ -75,8 +82,8 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
                                                          const float* kbar, const float* vhat,
                                                          uint16_t* kvc, int64_t L, uint32_t N) {
   using C = KvCfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_t[D][C::TP];
-  __shared__ __attribute__((aligned(16))) uint16_t v_t[D][C::TP];
+  __shared__ __attribute__((aligned(16))) char k_s[BLK * C::ROW];
+  __shared__ __attribute__((aligned(16))) char v_s[BLK * C::ROW];
   const uint32_t item = blockIdx.x;  // bh * N + j
   const uint32_t j = item % N;
   const size_t bh = item / N;
@@ -93,11 +100,9 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
       kw = *reinterpret_cast<const u32x4*>(kb + (size_t)t * D + 8 * sg);
       vw = *reinterpret_cast<const u32x4*>(vb + (size_t)t * D + 8 * sg);
     }
-#pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
-      k_t[8 * sg + e8][t] = (uint16_t)((kw[e8 / 2] >> (16 * (e8 % 2))) & 0xffffu);
-      v_t[8 * sg + e8][t] = (uint16_t)((vw[e8 / 2] >> (16 * (e8 % 2))) & 0xffffu);
-    }
+    const int off = t * C::ROW + ((sg ^ kv_swz(t, C::SEGS)) * 16);
+    *reinterpret_cast<u32x4*>(k_s + off) = kw;
+    *reinterpret_cast<u32x4*>(v_s + off) = vw;
   }
   __syncthreads();
 
@@ -105,23 +110,30 @@ __global__ __launch_bounds__(256) void kv_moments_kernel(const uint16_t* k, cons
   const float* vs = vhat + (size_t)item * D;
   const int wave = tid / kWave, lane = tid % kWave;
   const int h = lane / 32, l32 = lane % 32;
+  const int g = lane / 16, jj = lane % 16, r0 = 4 * (g / 2) + jj / 4;
+  // transposed fragment of dimension tile t, k-step kk
+  auto frag = [&](const char* tile, int t, int kk) -> bf16x8 {
+    const int col = 32 * t + 16 * (g % 2) + 4 * (jj % 4);
+    const char* p0 = tile + (16 * kk + r0) * C::ROW +
+                     ((col / 8) ^ kv_swz(r0, C::SEGS)) * 16 + (col % 8) * 2;
+    typedef __attribute__((address_space(3))) kv_v4i16 lds_v4i16;
+    const kv_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+    const kv_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * C::ROW));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   for (int tile = wave; tile < C::TD * C::TD; tile += C::WAVES) {
     const int ta = tile / C::TD, tb = tile % C::TD;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) acc = mfma32x32x16(frag(k_s, ta, kk), frag(v_s, tb, kk), acc);
     // pooled values first (a later load would otherwise wait for the stores)
     const float vb_sum = vs[32 * tb + l32];
     f32x4 m[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
       m[r4] = *reinterpret_cast<const f32x4*>(km + 32 * ta + 8 * r4 + 4 * h);
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_t[32 * ta + l32][16 * ks + 8 * h]);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&v_t[32 * tb + l32][16 * ks + 8 * h]);
-      acc = mfma32x32x16(a, b, acc);
-    }
     // lane: value dim b = 32 tb + l32; key dims a = 32 ta + mfma_row(r, h),
     // four consecutive per group of four registers
     uint16_t* orow = kvc + ((size_t)item * D + 32 * tb + l32) * D + 32 * ta;
