@@ -534,6 +534,10 @@ def main() -> int:
 
     # pooled-stage algorithmic bytes: Q, K, V read once, Qbar/Kbar/Vhat written
     pool_bytes = 3.0 * B * H * L * d * 2 + 3.0 * B * H * N * d * 4
+    # moments and thresholds, algorithmic bytes: Kbar and Qbar read once, the
+    # mean and the d x d second moment written and read back, tau written
+    moments_bytes = (2.0 * B * H * N * d * 4 + 2.0 * B * H * (d * d + d) * 4
+                     + 1.0 * B * H * N * 4)
 
     result = {
         "metric": METRIC,
@@ -561,6 +565,8 @@ def main() -> int:
         "fwd_executed_tflops": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12,
         "dense_equivalent_tflops": dense_equiv / (t["total_ms"] * 1e-3) / 1e12,
         "pool_hbm_gbps": pool_bytes / (t["pool_ms"] * 1e-3) / 1e9,
+        "moments_us": t["moments_ms"] * 1e3,
+        "moments_gbps": moments_bytes / (t["moments_ms"] * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "kernel": f"attn_kernel<{d},{w.block},fused> (solattn_fwd)",
                      "achieved": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
