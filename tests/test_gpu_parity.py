@@ -245,6 +245,21 @@ def test_fused_at_beta_minus_inf_equals_dense_kernel(sa):
     assert torch.equal(fused, dense)
 
 
+def test_exact_only_at_the_beta_limits(sa):
+    # beta = -inf: every block is exact, so dropping the approximation changes
+    # nothing and the output equals the dense kernel's bit for bit; beta = +inf:
+    # nothing is selected, and a row with no exact block outputs zeros
+    w = synth.WORKLOADS["image"].replace(H=3, L=4000, grid=(1, 50, 80))
+    q, k, v = (to_dev_bf16(x) for x in synth.make_inputs(w))
+    every = sa.forward(q, k, v, beta=-math.inf, block=w.block, chunk=w.chunk, exact_only=True)
+    dense = sa.dense_forward(q, k, v, block=w.block)
+    none = torch.full_like(q, float("nan"))
+    sa.forward(q, k, v, beta=math.inf, block=w.block, chunk=w.chunk, exact_only=True, out=none)
+    torch.cuda.synchronize()
+    assert torch.equal(every, dense)
+    assert torch.count_nonzero(none).item() == 0
+
+
 def test_chunk_size_does_not_change_selection(sa):
     w = synth.WORKLOADS["image"].replace(H=4)
     q, k, v = synth.make_inputs(w)
