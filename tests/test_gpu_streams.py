@@ -47,26 +47,30 @@ def test_forward_on_a_side_stream_is_bitwise_equal(sa):
     assert torch.equal(out, base)
 
 
-@pytest.mark.parametrize("beta", [1.0, -math.inf])
-def test_forward_replayed_from_a_graph_is_bitwise_equal(sa, beta):
+@pytest.mark.parametrize("first_order,beta", [(False, 1.0), (False, -math.inf), (True, 1.0)])
+def test_forward_replayed_from_a_graph_is_bitwise_equal(sa, first_order, beta):
     q, k, v = inputs(WORK)
     B, H, L, d = q.shape
     p = sa.problem(B, H, L, d, WORK.block, WORK.chunk, beta)
-    eager = sa.forward(q, k, v, beta=beta, block=WORK.block, chunk=WORK.chunk)
+    kw = dict(beta=beta, block=WORK.block, chunk=WORK.chunk)
+    fwd = sa.forward_first_order if first_order else sa.forward
+    eager = fwd(q, k, v, **kw)
     torch.cuda.synchronize()
-    # buffers of the captured call are allocated before capture
-    ws = sa.Workspace(p, "cuda")
-    out = torch.empty_like(q)
+    # every buffer of the captured call is allocated before capture
+    bufs = dict(out=torch.empty_like(q), ws=sa.Workspace(p, "cuda"))
+    if first_order:
+        bufs["fws"] = sa.FirstOrderWorkspace(p, "cuda")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):  # one eager call on the capture stream first
-        sa.forward(q, k, v, beta=beta, block=WORK.block, chunk=WORK.chunk, out=out, ws=ws)
+    with torch.cuda.stream(side):  # one eager call on a side stream first
+        fwd(q, k, v, **kw, **bufs)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        sa.forward(q, k, v, beta=beta, block=WORK.block, chunk=WORK.chunk, out=out, ws=ws)
+        fwd(q, k, v, **kw, **bufs)
     torch.cuda.synchronize()
+    out, ws = bufs["out"], bufs["ws"]
     noise = torch.randn(1 << 20, device="cuda")
     for replay in range(3):
         out.zero_()
