@@ -407,6 +407,8 @@ def main() -> int:
                          "Wan's 40 is one GPU's share when heads are split over eight")
     ap.add_argument("--beta", type=float, default=1.0)
     ap.add_argument("--skip-dense", action="store_true")
+    ap.add_argument("--skip-graph", action="store_true",
+                    help="skip timing the whole call replayed from a HIP graph")
     ap.add_argument("--skip-sweep", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--study", choices=("accuracy", "seq", "routing", "first-order"),
@@ -520,6 +522,29 @@ def main() -> int:
                     total_min_ms=float(np.min(tot)), fwd_median_ms=float(np.median(fwd)),
                     total_median_ms=float(np.median(tot)))
 
+    def time_graph(beta, steps):
+        """The whole call (pool, moments, fused kernel) captured once into a HIP
+        graph and replayed: the time without host launch overhead."""
+        p, ws = make(beta)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(p, ws)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(p, ws)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     beta = args.beta
     sel = selection(beta)
     ex, tile, apx = executed_flops(sel, L, d, w.block)
@@ -575,6 +600,12 @@ def main() -> int:
                      "traffic": measured_traffic()
                      if (w.name, w.block, w.H, beta) == ("wan", 128, 40, 1.0) else None},
     }
+
+    if not args.skip_graph:
+        g_ms = time_graph(beta, args.steps)
+        result["graph_replay_ms_per_call"] = g_ms
+        result["graph_replay_executed_tflops"] = fwd_flops / (g_ms * 1e-3) / 1e12
+        log(f"graph replay: {g_ms:.4f} ms per call")
 
     if not args.skip_dense:
         p = sa.problem(B, H, L, d, w.block, w.chunk, beta)
