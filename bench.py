@@ -36,7 +36,9 @@ from free_dynamic_sparse_amd import synth  # noqa: E402
 METRIC = "Sol-Attn fwd ms/call + executed TFLOP/s, 40h x L75.6k x d128 bf16, beta=1.0"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (vendor figure)
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_attn_fused_wan.json")
-ATTN_SOURCE = os.path.join(ROOT, "free_dynamic_sparse_amd", "csrc", "attn.hip")
+# the fused kernel's translation unit: the counters hold only while these are unchanged
+KERNEL_SOURCES = [os.path.join(ROOT, "free_dynamic_sparse_amd", "csrc", f)
+                  for f in ("attn.hip", "common.hpp", "launch.hpp")]
 
 
 def log(msg: str) -> None:
@@ -66,9 +68,12 @@ def executed_flops(sel: np.ndarray, L: int, d: int, block: int):
     return exact, tile, approx
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -79,7 +84,7 @@ def measured_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("attn_source_sha256_16") != source_hash(ATTN_SOURCE):
+    if t.get("kernel_sources_sha256_16") != source_hash(KERNEL_SOURCES):
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -26,18 +26,22 @@ __device__ __forceinline__ uint32_t xcd_contiguous_item(uint32_t bid, uint32_t t
   return x * q + (x < r ? x : r) + s;
 }
 
-// Head-striped schedule for the attention kernels: at any time every XCD
-// works on the same (b, h), XCD x on the contiguous query-block slab
-// [x*per, (x+1)*per) with per = ceil(N / 8).  One head's K and V then stay
-// resident in the shared last-level cache while each XCD's L2 sees
-// neighbouring query blocks, whose selected key blocks overlap.  The grid
-// has 8 * per * BH workgroups; a workgroup whose slab slot lies past N has no
-// item (returns false).
+// Head-striped schedule for the attention kernels: every XCD works through
+// the (b, h) in the same order, XCD x taking for (b, h) = bh the contiguous
+// query-block slab s = (x + bh) mod 8, items [s*per, (s+1)*per) with
+// per = ceil(N / 8).  One head's K and V then stay resident in the shared
+// last-level cache while each XCD's L2 sees neighbouring query blocks, whose
+// selected key blocks overlap.  Rotating the slab with bh gives every XCD
+// each slab equally often: where the work per query block depends on its
+// position (sparsity varies along the sequence), a fixed slab per XCD would
+// leave the XCDs with unequal totals and the whole launch waiting for the
+// busiest one.  The grid has 8 * per * BH workgroups; a workgroup whose slab
+// slot lies past N has no item (returns false).
 __device__ __forceinline__ bool head_striped_item(uint32_t bid, uint32_t N, uint32_t per,
                                                   uint32_t* bh, uint32_t* i) {
   const uint32_t x = bid % kXcds, slot = bid / kXcds;
   *bh = slot / per;
-  *i = x * per + (slot - *bh * per);
+  *i = ((x + *bh) % kXcds) * per + (slot - *bh * per);
   return *i < N;
 }
 

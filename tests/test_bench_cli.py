@@ -49,10 +49,16 @@ def test_traffic_is_used_only_for_the_source_it_was_measured_on(tmp_path, monkey
     src = tmp_path / "attn.hip"
     src.write_text("kernel source\n")
     prof = tmp_path / "traffic.json"
-    prof.write_text(json.dumps({"attn_source_sha256_16": bench.source_hash(str(src)),
+    hdr = tmp_path / "common.hpp"
+    hdr.write_text("helpers\n")
+    prof.write_text(json.dumps({"kernel_sources_sha256_16": bench.source_hash([str(src), str(hdr)]),
                                 "hbm_bytes_per_launch": 123}))
-    monkeypatch.setattr(bench, "ATTN_SOURCE", str(src))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src), str(hdr)])
     monkeypatch.setattr(bench, "PROFILE_TRAFFIC", str(prof))
+    assert bench.measured_traffic() == 123
+    hdr.write_text("helpers, changed\n")
+    assert bench.measured_traffic() is None
+    hdr.write_text("helpers\n")
     assert bench.measured_traffic() == 123
     src.write_text("kernel source, changed\n")
     assert bench.measured_traffic() is None
