@@ -89,34 +89,47 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w: synth.Workload, beta: float, heads: int = 3):
-    """The CPU oracle on the first `heads` heads of the workload (pooling,
-    moments, thresholds, selection and every query block's output): a
-    bounded sample of about 10-20 s of host work, scaled to executed TFLOP/s."""
+def cpu_baseline(w: synth.Workload, beta: float, out_heads: int = 4):
+    """The CPU oracle on a bounded sample of the workload, as planned for the
+    long video shapes: pooling, moments, thresholds and the whole selection
+    on every head, the output of every query block on the first out_heads
+    heads (about 10-30 s of host work); the whole-workload time is the
+    measured routing time plus the output time scaled by H / out_heads,
+    labelled as an extrapolation.  The oracle runs as it stands (float64
+    NumPy), with BLAS on every host thread it is given."""
     from threadpoolctl import threadpool_info
 
     from oracle import solattn_ref as ref
 
-    heads = min(heads, w.H)
-    flops, dt = 0.0, 0.0
-    for h in range(heads):
+    out_heads = min(out_heads, w.H)
+    t_route, t_out, flops_all, flops_out = 0.0, 0.0, 0.0, 0.0
+    for h in range(w.H):
         q, k, v = synth.make_head(w, 0, h)
         t0 = time.perf_counter()
         r = ref.solattn_head(q, k, v, beta, w.block, rows=[])
-        for i in range(w.N):
-            ref.forward_block(q, k, v, r.kbar, r.vhat, r.sel[i], i, w.block, r.scale)
-        dt += time.perf_counter() - t0
-        ex, tile, ap = executed_flops(r.sel[None], w.L, w.d, w.block)
-        flops += ex + tile + ap
+        t_route += time.perf_counter() - t0
+        f = ref.executed_flops(w.L, w.d, w.block, r.sel)
+        flops_all += f
+        if h < out_heads:
+            t0 = time.perf_counter()
+            for i in range(w.N):
+                ref.forward_block(q, k, v, r.kbar, r.vhat, r.sel[i], i, w.block, r.scale)
+            t_out += time.perf_counter() - t0
+            flops_out += f
+    t_all = t_route + t_out * w.H / out_heads
     threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s (executed)",
+    return {"value": flops_all / t_all / 1e12, "unit": "TFLOP/s (executed)",
             "cores": int(threads), "kind": "oracle",
-            "sample": f"heads 0-{heads - 1} of {w.H} at beta={beta}: pooling, moments, "
-                      f"thresholds, selection and all {w.N} query blocks' outputs per head, "
-                      f"float64 NumPy; {dt:.1f} s",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0)),
-            "extrapolated_seconds_all_heads": dt * w.H / heads,
-            "extrapolation": f"measured seconds x {w.H}/{heads} heads (an estimate, not measured)"}
+            "sample": f"{w.name} at beta={beta}: pooling, moments, thresholds and selection on "
+                      f"all {w.H} heads ({t_route:.1f} s), every query block's output on heads "
+                      f"0-{out_heads - 1} ({t_out:.1f} s); float64 NumPy",
+            "measured_seconds": t_route + t_out,
+            "routing_seconds_all_heads": t_route, "output_seconds_sampled_heads": t_out,
+            "output_tflops_sampled_heads": flops_out / t_out / 1e12 if t_out > 0 else None,
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "extrapolated_seconds_all_heads": t_all,
+            "extrapolation": f"routing measured on all heads + output seconds x {w.H}/{out_heads} "
+                             f"heads (an estimate, not measured); value uses it"}
 
 
 def _to_device(w: synth.Workload):
@@ -167,7 +180,7 @@ def accuracy_study(sa, w: synth.Workload, betas=(0.0, 0.5, 1.0, 1.5, 2.0, 3.0, m
             ws = sa.Workspace(p, debug=True)
             sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
             sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
-            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue, ws.sel_mask,
                            ws.sel_count)
             torch.cuda.synchronize()
             row["density"] = float(ws.sel_count.double().mean().item()) / w.N
@@ -175,7 +188,7 @@ def accuracy_study(sa, w: synth.Workload, betas=(0.0, 0.5, 1.0, 1.5, 2.0, 3.0, m
             row[mode] = {"rel_l2_mean": float(rel.mean()), "rel_l2_max": float(rel.max()),
                          "cosine_mean": float(cos.mean()), "cosine_min": float(cos.min()),
                          "fwd_ms": _time_ms(lambda: sa.solattn_fwd(
-                             p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out), 5)}
+                             p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue), 5)}
         row["approx_overhead"] = row["full"]["fwd_ms"] / row["exact_only"]["fwd_ms"] - 1.0
         rows.append(row)
         log(f"accuracy {row}")
@@ -210,7 +223,7 @@ def first_order_study(sa, w: synth.Workload, betas=(0.5, 1.0, 1.5, math.inf)):
         def zeroth():
             sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
             sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
-            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out)
+            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue)
 
         def first():
             sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
@@ -221,7 +234,7 @@ def first_order_study(sa, w: synth.Workload, betas=(0.5, 1.0, 1.5, math.inf)):
 
         sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
         sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
-        sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+        sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue, ws.sel_mask,
                        ws.sel_count)
         torch.cuda.synchronize()
         unsel = (w.N - ws.sel_count.double().cpu()).reshape(B * H, w.N)
@@ -236,7 +249,7 @@ def first_order_study(sa, w: synth.Workload, betas=(0.5, 1.0, 1.5, math.inf)):
                          "rel_l2_per_head": [round(float(x), 5) for x in rel],
                          "ms_per_call": _time_ms(fn, 3)}
         pe = sa.problem(B, H, L, d, w.block, w.chunk, beta, None, True)
-        sa.solattn_fwd(pe, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out)
+        sa.solattn_fwd(pe, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue)
         torch.cuda.synchronize()
         rel, cos = _errors(out, dense)
         row["exact_only"] = {"rel_l2_mean": float(rel.mean()), "cosine_mean": float(cos.mean()),
@@ -274,7 +287,7 @@ def seq_study(sa):
             ws = sa.Workspace(p, debug=True)
             sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
             sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
-            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+            sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue, ws.sel_mask,
                            ws.sel_count)
             torch.cuda.synchronize()
             density = float(ws.sel_count.double().mean().item()) / w.N
@@ -282,7 +295,7 @@ def seq_study(sa):
                                    sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov,
                                                       ws.tau),
                                    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau,
-                                                  out)), 3)
+                                                  out, ws.queue)), 3)
             row = {"L": L, "beta": beta, "density": density, "sparsity": 1.0 - density,
                    "ms_per_call": ms, "dense_ms": dense_ms, "speedup_vs_dense": dense_ms / ms}
             rows.append(row)
@@ -322,7 +335,7 @@ def routing_study(sa, w: synth.Workload, beta: float):
     ws = sa.Workspace(p, debug=True)
     sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
     sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
-    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask, ws.sel_count)
+    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue, ws.sel_mask, ws.sel_count)
     torch.cuda.synchronize()
     dens_thr = ws.sel_count.double().cpu().numpy() / N
     rho = float(dens_thr.mean())
@@ -332,7 +345,7 @@ def routing_study(sa, w: synth.Workload, beta: float):
     ws_inf = sa.Workspace(p_inf)
     sa.solattn_moments(p_inf, ws.qbar, ws.kbar, ws_inf.kmean, ws_inf.kcov, ws_inf.tau)
     t_pass = _time_ms(lambda: sa.solattn_fwd(p_inf, q, k, v, ws.qbar, ws.kbar, ws.vhat,
-                                             ws_inf.tau, out), 5)
+                                             ws_inf.tau, out, ws.queue), 5)
     dense = torch.empty_like(q)
     sa.solattn_dense_fwd(sa.problem(B, H, L, d, w.block, w.chunk, -math.inf), q, k, v, dense)
     p_eo = sa.problem(B, H, L, d, w.block, w.chunk, beta, None, True)
@@ -342,9 +355,9 @@ def routing_study(sa, w: synth.Workload, beta: float):
         res = {}
         for mode, pp in (("full", p), ("exact_only", p_eo)):
             if sel_mask is None:
-                sa.solattn_fwd(pp, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out)
+                sa.solattn_fwd(pp, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue)
             else:
-                sa.solattn_fwd_masked(pp, q, k, v, ws.kbar, ws.vhat, sel_mask, out)
+                sa.solattn_fwd_masked(pp, q, k, v, ws.kbar, ws.vhat, sel_mask, out, ws.queue)
             torch.cuda.synchronize()
             rel, cos = _errors(out, dense)
             res[mode] = {"rel_l2_mean": float(rel.mean()), "cosine_mean": float(cos.mean())}
@@ -495,7 +508,7 @@ def main() -> int:
         sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau)
         if ev is not None:
             ev[2].record(stream)
-        sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+        sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue, ws.sel_mask,
                        ws.sel_count)
         if ev is not None:
             ev[3].record(stream)

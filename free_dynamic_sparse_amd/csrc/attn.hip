@@ -45,6 +45,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -114,10 +116,12 @@ struct AttnArgs {
   float* out_f32;          // if set: O in float32 here instead of bf16 in out
   float* lse2;             // if set: per row, log2 of the softmax denominator in logit units
                            // (m + log2 l, the scale of the 2^(c s - m) weights)
+  uint32_t* queue;   // fused kernel: kXcds work-queue counters, kQueueStride apart
   int64_t L;
   uint32_t N;
   uint32_t pairs;    // ceil(N / 2)
   uint32_t per_xcd;  // pairs per XCD slab: ceil(pairs / 8)
+  uint32_t queue_len;  // entries per work queue: B * H * per_xcd
   float scale;
   float c_log2;      // scale * log2(e): logits enter exp2 in this unit
   uint32_t exact_only;
@@ -731,19 +735,73 @@ __device__ __forceinline__ void route_approx_phase(
 
 // ------------------------------------------------------------------ kernel
 
+// ------------------------------------------------------------- work queue
+
+// Work items of the fused kernel are pairs of query blocks.  They are dealt
+// to kXcds queues in the head-striped order of head_striped_item (queue x
+// holds, head after head, the slab (x + bh) mod 8 of the head's pairs), so a
+// queue's items are neighbouring query blocks of one head at a time.  A
+// persistent workgroup of XCD x (workgroup id mod 8, the order in which the
+// dispatcher deals workgroups to XCDs) takes items from queue x with an
+// atomic counter, in order, and once that queue is empty from the others in
+// turn.  Query-dependent budgets make items unequal; a workgroup that
+// finishes early takes the next item at once, and no CU waits for a
+// workgroup to be dispatched.  An item is computed the same way wherever it
+// runs, so the output does not depend on which workgroup takes it.
+constexpr uint32_t kQueueStride = 32;  // u32 between counters: one 128-byte line each
+constexpr uint32_t kNoItem = 0xFFFFFFFFu;
+
+struct WorkQueue {
+  uint32_t* ctr;
+  uint32_t len;    // entries per queue (bh count * per)
+  uint32_t per;    // pairs per slab
+  uint32_t pairs;  // pairs per head
+  // Next item (bh * pairs + pair) for a workgroup of XCD home, or kNoItem.
+  __device__ uint32_t take(uint32_t home) const {
+    for (uint32_t v = 0; v < kXcds; ++v) {
+      const uint32_t qx = (home + v) % kXcds;
+      for (;;) {
+        const uint32_t idx = __hip_atomic_fetch_add(ctr + qx * kQueueStride, 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (idx >= len) break;
+        const uint32_t bh = idx / per, slot = idx - bh * per;
+        const uint32_t pair = ((qx + bh) % kXcds) * per + slot;
+        if (pair < pairs) return bh * pairs + pair;
+      }
+    }
+    return kNoItem;
+  }
+};
+
+__global__ void queue_reset_kernel(uint32_t* ctr) {
+  if (threadIdx.x < kXcds)
+    __hip_atomic_store(ctr + threadIdx.x * kQueueStride, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------ kernels
+
+// x, through an empty volatile asm: the compiler cannot move what is derived
+// from it out of the loop the asm sits in.  Per-lane offsets derived from the
+// thread id inside a persistent loop are then recomputed per item instead of
+// occupying registers across the whole loop.
+__device__ __forceinline__ int loop_local(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// One work item: the query-block pair (2 pair, 2 pair + 1) of head bh.
 template <int D, int BLK, bool FUSED>
-__global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_t bh,
+                                          uint32_t pair) {
   using C = Cfg<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) char smem[FUSED ? C::SMEM_FUSED : C::SMEM_DENSE];
   auto selbits = reinterpret_cast<uint32_t(*)[kMaxBlocks / 32]>(smem + C::BITS);
   auto qbar_s = reinterpret_cast<float(*)[D]>(smem + C::QBAR);
 
-  const int tid = threadIdx.x, lane = tid % kWave;
+  const int tid = loop_local((int)threadIdx.x), lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int grp = wave / C::QW;  // which block of the pair
   const int h = lane / 32, l32 = lane % 32;
-  uint32_t bh, pair;
-  if (!head_striped_item(blockIdx.x, a.pairs, a.per_xcd, &bh, &pair)) return;
   const uint32_t N = a.N;
   const uint32_t i_g = 2 * pair + grp;  // this group's query block
   const bool grp_on = i_g < N;          // block 2p+1 may not exist
@@ -872,25 +930,101 @@ __global__ __launch_bounds__(4 * BLK) void attn_kernel(AttnArgs a) {
   }
 }
 
+// The dense comparison kernel: one workgroup per item, head-striped.
+template <int D, int BLK>
+__global__ __launch_bounds__(4 * BLK) void attn_dense_kernel(AttnArgs a) {
+  using C = Cfg<D, BLK>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_DENSE];
+  uint32_t bh, pair;
+  if (!head_striped_item(blockIdx.x, a.pairs, a.per_xcd, &bh, &pair)) return;
+  attn_item<D, BLK, false>(a, smem, bh, pair);
+}
+
+// The fused Sol-Attn kernel: persistent workgroups draining the work queues.
+// The next item is taken while the current one runs and handed to the whole
+// workgroup through LDS at the item's end.
+template <int D, int BLK>
+__global__ __launch_bounds__(4 * BLK) void attn_fused_kernel(AttnArgs a) {
+  using C = Cfg<D, BLK>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_FUSED + 16];
+  uint32_t* slot = reinterpret_cast<uint32_t*>(smem + C::SMEM_FUSED);
+  const WorkQueue wq{a.queue, a.queue_len, a.per_xcd, a.pairs};
+  const uint32_t home = blockIdx.x % kXcds;
+  if (threadIdx.x == 0) slot[0] = wq.take(home);
+  __syncthreads();
+  uint32_t item = slot[0];
+  while (item != kNoItem) {
+    uint32_t next = kNoItem;
+    if (threadIdx.x == 0) next = wq.take(home);
+    const uint32_t bh = item / a.pairs;
+    attn_item<D, BLK, true>(a, smem, bh, item - bh * a.pairs);
+    __syncthreads();  // every wave has read slot[0]
+    if (threadIdx.x == 0) slot[0] = next;
+    __syncthreads();
+    item = slot[0];
+  }
+}
+
+// Workgroups of the persistent fused kernel on the current device: every CU
+// times the kernel's occupancy, found once per device and instantiation.
+// Plain static storage (no allocation), so the allocation-free entry point
+// can use it too.
+constexpr int kMaxDevices = 64;
+std::mutex g_grid_mu;
+int g_grid[kMaxDevices][4];
+
+hipError_t persistent_grid(const void* kernel, int threads, int inst, uint32_t* grid) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_grid_mu);
+  if (g_grid[dev][inst] == 0) {
+    int cus = 0, occ = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0);
+    if (e != hipSuccess) return e;
+    g_grid[dev][inst] = (cus > 0 ? cus : 1) * (occ > 0 ? occ : 1);
+  }
+  *grid = (uint32_t)g_grid[dev][inst];
+  return hipSuccess;
+}
+
 template <bool FUSED>
 hipError_t launch_attn(const Shape& s, AttnArgs a, hipStream_t stream) {
   a.L = s.L;
   a.N = (uint32_t)s.N;
   a.pairs = (uint32_t)((s.N + 1) / 2);
   a.per_xcd = (a.pairs + kXcds - 1) / kXcds;
+  a.queue_len = (uint32_t)(s.bh * a.per_xcd);
   a.scale = s.scale;
   a.c_log2 = s.scale * kLog2e;
-  const dim3 grid((uint32_t)(kXcds * a.per_xcd * s.bh));
-#define SOLATTN_LAUNCH(DD, BB)                                                               \
-  if (s.d == DD && s.block == BB) {                                                          \
-    hipLaunchKernelGGL((attn_kernel<DD, BB, FUSED>), grid, dim3(Cfg<DD, BB>::NT), 0, stream, \
-                       a);                                                                   \
-    return hipGetLastError();                                                                \
+  const uint64_t items = (uint64_t)s.bh * a.pairs;
+#define SOLATTN_LAUNCH(DD, BB, INST)                                                           \
+  if (s.d == DD && s.block == BB) {                                                            \
+    if (!FUSED) {                                                                              \
+      const dim3 grid((uint32_t)(kXcds * a.per_xcd * s.bh));                                   \
+      hipLaunchKernelGGL((attn_dense_kernel<DD, BB>), grid, dim3(Cfg<DD, BB>::NT), 0, stream,  \
+                         a);                                                                   \
+      return hipGetLastError();                                                                \
+    }                                                                                          \
+    uint32_t grid = 0;                                                                         \
+    hipError_t e = persistent_grid(reinterpret_cast<const void*>(&attn_fused_kernel<DD, BB>),  \
+                                   Cfg<DD, BB>::NT, INST, &grid);                              \
+    if (e != hipSuccess) return e;                                                             \
+    if (items < grid) grid = (uint32_t)items;                                                  \
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(kWave), 0, stream, a.queue);          \
+    e = hipGetLastError();                                                                     \
+    if (e != hipSuccess) return e;                                                             \
+    hipLaunchKernelGGL((attn_fused_kernel<DD, BB>), dim3(grid), dim3(Cfg<DD, BB>::NT), 0,      \
+                       stream, a);                                                             \
+    return hipGetLastError();                                                                  \
   }
-  SOLATTN_LAUNCH(128, 128)
-  SOLATTN_LAUNCH(128, 64)
-  SOLATTN_LAUNCH(64, 128)
-  SOLATTN_LAUNCH(64, 64)
+  SOLATTN_LAUNCH(128, 128, 0)
+  SOLATTN_LAUNCH(128, 64, 1)
+  SOLATTN_LAUNCH(64, 128, 2)
+  SOLATTN_LAUNCH(64, 64, 3)
 #undef SOLATTN_LAUNCH
   return hipErrorInvalidValue;
 }
@@ -899,11 +1033,14 @@ hipError_t launch_attn(const Shape& s, AttnArgs a, hipStream_t stream) {
 
 int64_t fused_max_blocks() { return kMaxBlocks; }
 
+size_t fwd_workspace_bytes() { return (size_t)kXcds * kQueueStride * sizeof(uint32_t); }
+
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,
                       const uint64_t* sel_in, void* out, uint64_t* sel_mask, int32_t* sel_count,
-                      float* out_f32, float* lse2, hipStream_t stream) {
+                      float* out_f32, float* lse2, void* workspace, hipStream_t stream) {
   AttnArgs a{};
+  a.queue = static_cast<uint32_t*>(workspace);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);

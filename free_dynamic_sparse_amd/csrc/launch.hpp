@@ -28,14 +28,19 @@ hipError_t launch_moments(const Shape& s, const float* qbar, const float* kbar, 
 // Largest N = ceil(L / block) the fused kernel keeps on-chip selection bits for.
 int64_t fused_max_blocks();
 
+// Device workspace of the fused kernel (its work-queue counters), in bytes;
+// the same for every problem.
+size_t fwd_workspace_bytes();
+
 // sel_in null: threshold routing from qbar and tau.  Otherwise the given
 // selections (qbar and tau unused).  out_f32, if set, receives O in float32
 // instead of out; lse2, if set, the log2 of each row's softmax denominator in
-// units of scale * log2(e) * q.k (f32 [bh, L]).
+// units of scale * log2(e) * q.k (f32 [bh, L]).  workspace: fwd_workspace_bytes()
+// of device memory, 256-byte aligned, reset in-stream by every launch.
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v,
                       const float* qbar, const float* kbar, const float* vhat, const float* tau,
                       const uint64_t* sel_in, void* out, uint64_t* sel_mask, int32_t* sel_count,
-                      float* out_f32, float* lse2, hipStream_t stream);
+                      float* out_f32, float* lse2, void* workspace, hipStream_t stream);
 
 // First-order term of the unselected blocks.
 // kvc[bh][j][b][a] = sum over block j's valid tokens t of v_t[b] (k_t[a] - Kbar_j[a]), bf16,

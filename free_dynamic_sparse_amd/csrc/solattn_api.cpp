@@ -14,6 +14,7 @@ constexpr int64_t kMaxSeqLen = int64_t(1) << 22;
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 bool ok_opt_ptr(const void* p) { return p == nullptr || aligned16(p); }
 
@@ -52,19 +53,27 @@ int check_routing(const solattn_problem_t* p) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? SOLATTN_OK : SOLATTN_E_HIP; }
 
+// The fused forward's workspace: its work-queue counters.
+int check_workspace(const void* ws, size_t bytes, size_t need) {
+  if (ws == nullptr || !aligned256(ws) || bytes < need) return SOLATTN_E_WORKSPACE;
+  return SOLATTN_OK;
+}
+
 // Regions of the first-order workspace, each starting on a 256-byte boundary:
-// the fused kernel's selection bitmaps (u64 [bh, N, ceil(N/64)]), its per-row
-// log2 denominators (f32 [bh, L]) and its float32 output (f32 [bh, L, d]).
+// the fused kernel's work-queue counters, its selection bitmaps
+// (u64 [bh, N, ceil(N/64)]), its per-row log2 denominators (f32 [bh, L]) and
+// its float32 output (f32 [bh, L, d]).
 struct FirstOrderLayout {
-  size_t sel, lse2, o32, total;
+  size_t queue, sel, lse2, o32, total;
 };
 
 FirstOrderLayout first_order_layout(const solattn::Shape& s) {
   auto up = [](size_t x) { return (x + 255u) & ~(size_t)255u; };
   const size_t w64 = (size_t)((s.N + 63) / 64);
   FirstOrderLayout l;
-  l.sel = 0;
-  l.lse2 = up((size_t)s.bh * (size_t)s.N * w64 * 8u);
+  l.queue = 0;
+  l.sel = up(solattn::fwd_workspace_bytes());
+  l.lse2 = l.sel + up((size_t)s.bh * (size_t)s.N * w64 * 8u);
   l.o32 = l.lse2 + up((size_t)s.bh * (size_t)s.L * 4u);
   l.total = l.o32 + up((size_t)s.bh * (size_t)s.L * (size_t)s.d * 4u);
   return l;
@@ -103,9 +112,17 @@ int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* 
                                           static_cast<hipStream_t>(stream)));
 }
 
+size_t solattn_fwd_workspace_bytes(const solattn_problem_t* p) {
+  solattn::Shape s;
+  bool empty = false;
+  if (check_shape(p, &s, &empty) != SOLATTN_OK || empty) return 0;
+  return solattn::fwd_workspace_bytes();
+}
+
 int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
                 const float* qbar, const float* kbar, const float* vhat, const float* tau,
-                void* out, uint64_t* sel_mask, int32_t* sel_count, void* stream) {
+                void* out, void* workspace, size_t workspace_bytes, uint64_t* sel_mask,
+                int32_t* sel_count, void* stream) {
   solattn::Shape s;
   bool empty = false;
   int rc = check_shape(p, &s, &empty);
@@ -118,14 +135,16 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
       !ok_ptr(vhat) || !ok_ptr(tau) || !ok_ptr(out) || !ok_opt_ptr(sel_mask) ||
       !ok_opt_ptr(sel_count))
     return SOLATTN_E_INVALID_ARG;
+  rc = check_workspace(workspace, workspace_bytes, solattn::fwd_workspace_bytes());
+  if (rc != SOLATTN_OK) return rc;
   return from_hip(solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, nullptr, out, sel_mask,
-                                      sel_count, nullptr, nullptr,
+                                      sel_count, nullptr, nullptr, workspace,
                                       static_cast<hipStream_t>(stream)));
 }
 
 int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k, const void* v,
                        const float* kbar, const float* vhat, const uint64_t* sel_in, void* out,
-                       void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream) {
   solattn::Shape s;
   bool empty = false;
   int rc = check_shape(p, &s, &empty);
@@ -135,8 +154,10 @@ int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k,
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(kbar) || !ok_ptr(vhat) ||
       !ok_ptr(sel_in) || !ok_ptr(out))
     return SOLATTN_E_INVALID_ARG;
+  rc = check_workspace(workspace, workspace_bytes, solattn::fwd_workspace_bytes());
+  if (rc != SOLATTN_OK) return rc;
   return from_hip(solattn::launch_fwd(s, q, k, v, nullptr, kbar, vhat, nullptr, sel_in, out,
-                                      nullptr, nullptr, nullptr, nullptr,
+                                      nullptr, nullptr, nullptr, nullptr, workspace,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -174,17 +195,18 @@ int solattn_fwd_first_order(const solattn_problem_t* p, const void* q, const voi
   if (s.N > solattn::fused_max_blocks()) return SOLATTN_E_UNSUPPORTED;
   if (empty) return SOLATTN_OK;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(qbar) || !ok_ptr(kbar) ||
-      !ok_ptr(vhat) || !ok_ptr(kvc) || !ok_ptr(tau) || !ok_ptr(out) || !ok_ptr(workspace))
+      !ok_ptr(vhat) || !ok_ptr(kvc) || !ok_ptr(tau) || !ok_ptr(out))
     return SOLATTN_E_INVALID_ARG;
   const FirstOrderLayout l = first_order_layout(s);
-  if (workspace_bytes < l.total) return SOLATTN_E_INVALID_ARG;
+  rc = check_workspace(workspace, workspace_bytes, l.total);
+  if (rc != SOLATTN_OK) return rc;
   char* ws = static_cast<char*>(workspace);
   uint64_t* sel = reinterpret_cast<uint64_t*>(ws + l.sel);
   float* lse2 = reinterpret_cast<float*>(ws + l.lse2);
   float* o32 = reinterpret_cast<float*>(ws + l.o32);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, nullptr, nullptr, sel,
-                                     nullptr, o32, lse2, st);
+                                     nullptr, o32, lse2, ws + l.queue, st);
   if (e != hipSuccess) return SOLATTN_E_HIP;
   return from_hip(solattn::launch_first_order(s, q, kbar, kvc, sel, lse2, o32, out, st));
 }
@@ -247,19 +269,22 @@ const char* solattn_strerror(int code) {
       return "ok";
     case SOLATTN_E_INVALID_ARG:
       return "invalid argument (null or misaligned pointer, bad shape, NaN beta or scale, "
-             "k < 1, top_p outside (0, 1], a first-order workspace too small, or the "
-             "first-order forward asked for in exact-only mode)";
+             "k < 1, top_p outside (0, 1], or the first-order forward asked for in "
+             "exact-only mode)";
     case SOLATTN_E_UNSUPPORTED:
       return "unsupported configuration (head_dim and block must be 64 or 128, chunk 1..64, "
              "and solattn_fwd and the top-k / top-p selections need ceil(seq_len / block) "
              "<= 8192)";
     case SOLATTN_E_HIP:
       return "HIP launch failed";
+    case SOLATTN_E_WORKSPACE:
+      return "workspace missing, not 256-byte aligned, or smaller than the entry point's "
+             "workspace size (solattn_fwd_workspace_bytes, solattn_fwd_first_order_workspace)";
     default:
       return "unknown error code";
   }
 }
 
-int solattn_version(void) { return 200; }
+int solattn_version(void) { return 300; }
 
 }  // extern "C"

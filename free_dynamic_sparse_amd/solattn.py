@@ -22,10 +22,11 @@ SOLATTN_OK = 0
 SOLATTN_E_INVALID_ARG = -1
 SOLATTN_E_UNSUPPORTED = -2
 SOLATTN_E_HIP = -3
+SOLATTN_E_WORKSPACE = -4
 SOLATTN_FLAG_EXACT_ONLY = 1
 
-EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_masked",
-           "solattn_dense_fwd",
+EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_workspace_bytes",
+           "solattn_fwd_masked", "solattn_dense_fwd",
            "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp",
            "solattn_kv_moments", "solattn_fwd_first_order", "solattn_fwd_first_order_workspace",
            "solattn_strerror", "solattn_version")
@@ -56,9 +57,12 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     pp = ctypes.POINTER(Problem)
     lib.solattn_pool.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_moments.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.solattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.solattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp,
+                                vp]
+    lib.solattn_fwd_workspace_bytes.argtypes = [pp]
+    lib.solattn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.solattn_dense_fwd.argtypes = [pp, vp, vp, vp, vp, vp]
-    lib.solattn_fwd_masked.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.solattn_fwd_masked.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.solattn_proxy_map.argtypes = [pp, vp, vp, vp, vp]
     lib.solattn_select_topk.argtypes = [pp, vp, ctypes.c_int64, vp, vp, vp]
     lib.solattn_select_topp.argtypes = [pp, vp, ctypes.c_float, vp, vp, vp]
@@ -151,9 +155,21 @@ def solattn_moments(p: Problem, qbar, kbar, kmean, kcov, tau, mu=None, sigma=Non
            "solattn_moments")
 
 
-def solattn_fwd(p: Problem, q, k, v, qbar, kbar, vhat, tau, out, sel_mask=None, sel_count=None,
-                stream=None) -> None:
+def _need_workspace(ws, name: str = "workspace") -> None:
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous 1-D uint8 CUDA tensor")
+
+
+def solattn_fwd_workspace_bytes(p: Problem) -> int:
+    return int(LIB.solattn_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def solattn_fwd(p: Problem, q, k, v, qbar, kbar, vhat, tau, out, workspace, sel_mask=None,
+                sel_count=None, stream=None) -> None:
+    """workspace: a contiguous uint8 CUDA tensor of at least
+    solattn_fwd_workspace_bytes(p) bytes (the work-queue counters)."""
     full, pooled, N = _dims(p)
+    _need_workspace(workspace)
     B, H = p.batch, p.heads
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
         _need(t, torch.bfloat16, full, n)
@@ -165,20 +181,22 @@ def solattn_fwd(p: Problem, q, k, v, qbar, kbar, vhat, tau, out, sel_mask=None, 
     if sel_count is not None:
         _need(sel_count, torch.int32, (B, H, N), "sel_count")
     _check(LIB.solattn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar), _ptr(kbar),
-                           _ptr(vhat), _ptr(tau), _ptr(out), _ptr(sel_mask), _ptr(sel_count),
-                           _stream(stream)), "solattn_fwd")
+                           _ptr(vhat), _ptr(tau), _ptr(out), _ptr(workspace), workspace.numel(),
+                           _ptr(sel_mask), _ptr(sel_count), _stream(stream)), "solattn_fwd")
 
 
-def solattn_fwd_masked(p: Problem, q, k, v, kbar, vhat, sel_in, out, stream=None) -> None:
+def solattn_fwd_masked(p: Problem, q, k, v, kbar, vhat, sel_in, out, workspace,
+                       stream=None) -> None:
     full, pooled, N = _dims(p)
+    _need_workspace(workspace)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
         _need(t, torch.bfloat16, full, n)
     for t, n in ((kbar, "kbar"), (vhat, "vhat")):
         _need(t, torch.float32, pooled, n)
     _need(sel_in, torch.int64, (p.batch, p.heads, N, (N + 63) // 64), "sel_in")
     _check(LIB.solattn_fwd_masked(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar),
-                                  _ptr(vhat), _ptr(sel_in), _ptr(out), _stream(stream)),
-           "solattn_fwd_masked")
+                                  _ptr(vhat), _ptr(sel_in), _ptr(out), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)), "solattn_fwd_masked")
 
 
 def solattn_kv_moments(p: Problem, k, v, kbar, vhat, kvc, stream=None) -> None:
@@ -207,9 +225,7 @@ def solattn_fwd_first_order(p: Problem, q, k, v, qbar, kbar, vhat, kvc, tau, out
         _need(t, torch.float32, pooled, n)
     _need(kvc, torch.bfloat16, (p.batch, p.heads, N, p.head_dim, p.head_dim), "kvc")
     _need(tau, torch.float32, (p.batch, p.heads, N), "tau")
-    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_cuda \
-            or not workspace.is_contiguous():
-        raise ValueError("workspace: expected a contiguous 1-D uint8 CUDA tensor")
+    _need_workspace(workspace)
     _check(LIB.solattn_fwd_first_order(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar),
                                        _ptr(kbar), _ptr(vhat), _ptr(kvc), _ptr(tau), _ptr(out),
                                        _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -272,6 +288,9 @@ class Workspace:
         self.sel_mask = (torch.empty((B, H, N, (N + 63) // 64), dtype=torch.int64, device=device)
                          if debug else None)
         self.sel_count = torch.empty((B, H, N), dtype=torch.int32, device=device) if debug else None
+        # the fused kernel's work-queue counters
+        self.queue = torch.empty(max(1, solattn_fwd_workspace_bytes(p)), dtype=torch.uint8,
+                                 device=device)
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0,
@@ -287,8 +306,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: float = 1.0
         out = torch.empty_like(q)
     solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, stream)
     solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma, stream)
-    solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask, ws.sel_count,
-                stream)
+    solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue, ws.sel_mask,
+                ws.sel_count, stream)
     return out
 
 
@@ -352,7 +371,7 @@ def forward_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel_mask: 
     if out is None:
         out = torch.empty_like(q)
     solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, stream)
-    solattn_fwd_masked(p, q, k, v, ws.kbar, ws.vhat, sel_mask, out, stream)
+    solattn_fwd_masked(p, q, k, v, ws.kbar, ws.vhat, sel_mask, out, ws.queue, stream)
     return out
 
 

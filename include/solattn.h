@@ -45,6 +45,7 @@ extern "C" {
 #define SOLATTN_E_INVALID_ARG (-1) /* null pointer, bad shape, NaN beta, misalignment */
 #define SOLATTN_E_UNSUPPORTED (-2) /* head_dim, block or chunk outside the built set */
 #define SOLATTN_E_HIP (-3)         /* a HIP launch failed; see hipGetLastError */
+#define SOLATTN_E_WORKSPACE (-4)   /* workspace NULL, not 256-byte aligned, or too small */
 
 /* solattn_problem_t.flags */
 #define SOLATTN_FLAG_EXACT_ONLY 1u /* drop the approximation of unselected blocks */
@@ -55,11 +56,14 @@ extern "C" {
  *  head_dim               d: 64 or 128.
  *  block                  tokens per block, 64 or 128 (the page uses square
  *                         block x block tiles for queries and keys alike).
- *  chunk                  C, pooled keys per routing chunk, 1..64.  C changes
- *                         the schedule, never the result (method section,
- *                         chunk-wise streaming thresholding); it is validated
- *                         and the fused kernel routes 64 pooled keys per step
- *                         whatever its value.
+ *  chunk                  C, pooled keys per routing chunk, 1..64.  On the
+ *                         page C changes the schedule, never the result
+ *                         (method section, chunk-wise streaming
+ *                         thresholding: the selected set is the union of
+ *                         the chunks' sets).  Here it is validated and has
+ *                         no other effect: the fused kernel routes 64 pooled
+ *                         keys per step whatever its value, and every output
+ *                         bit is the same for every C.
  *  beta                   standardized cutoff of tau_i = mu_i + beta*sigma_i
  *                         (Eq. 4).  Any finite value; -INFINITY selects every
  *                         block, +INFINITY none.  NaN is rejected.
@@ -123,10 +127,20 @@ int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* 
  *   kbar, vhat in:  f32 [B, H, N, d]  from solattn_pool (KC and VC chunks)
  *   tau        in:  f32 [B, H, N]     from solattn_moments
  *   out        out: bf16 [B, H, L, d]
+ *   workspace  device memory of workspace_bytes >= solattn_fwd_workspace_bytes(p)
+ *              bytes, 256-byte aligned, owned by the caller; its contents on
+ *              entry do not matter.  It holds the counters of the work queues
+ *              from which persistent workgroups take pairs of query blocks
+ *              (per-row budgets |S_i| depend on the query, method section,
+ *              Eq. 4, so items take unequal time); a kernel in the same
+ *              stream clears them at the start of every call, so the call
+ *              can be captured in a HIP graph.  Calls that share a workspace
+ *              and overlap race.  NULL, misaligned or too small:
+ *              SOLATTN_E_WORKSPACE.
  *   sel_mask   out, may be NULL: u64 [B, H, N, ceil(N/64)]; bit (j mod 64) of
  *              word j/64 of row (b, h, i) is set iff block j is in S_i.
  *   sel_count  out, may be NULL: i32 [B, H, N], |S_i|.
- * For query block i the kernel scans the pooled keys in chunks of C: the
+ * For query block i the kernel scans the pooled keys 64 at a time: the
  * proxy score shat_ij = scale*Qbar_i.Kbar_j is compared with tau_i on chip;
  * selected blocks get exact attention, unselected blocks the zeroth-order
  * term (n_j * exp(centre) in the denominator, exp(centre) * Vhat_j in the
@@ -139,7 +153,14 @@ int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* 
  */
 int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,
                 const float* qbar, const float* kbar, const float* vhat, const float* tau,
-                void* out, uint64_t* sel_mask, int32_t* sel_count, void* stream);
+                void* out, void* workspace, size_t workspace_bytes, uint64_t* sel_mask,
+                int32_t* sel_count, void* stream);
+
+/* Workspace bytes solattn_fwd and solattn_fwd_masked need (the same for
+ * every problem: 1 KiB); 0 for an empty or invalid problem, whose call needs
+ * none. */
+size_t solattn_fwd_workspace_bytes(const solattn_problem_t* p);
+
 
 /*
  * The fused forward with the selected sets given instead of routed: the
@@ -154,11 +175,12 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
  *              (e.g. from solattn_select_topk / solattn_select_topp); bits
  *              at or past N are ignored
  *   out        out: bf16 [B, H, L, d]
+ *   workspace  as for solattn_fwd
  * beta and chunk are ignored.  Same limit as solattn_fwd (N <= 8192).
  */
 int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k, const void* v,
                        const float* kbar, const float* vhat, const uint64_t* sel_in, void* out,
-                       void* stream);
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * First-order term of the unselected blocks.  The page expands an
@@ -188,18 +210,19 @@ int solattn_fwd_masked(const solattn_problem_t* p, const void* q, const void* k,
  *   q, k, v, qbar, kbar, vhat, tau, out  as for solattn_fwd
  *   kvc        in: bf16 [B, H, N, d, d] from solattn_kv_moments
  *   workspace  device scratch of workspace_bytes >=
- *              solattn_fwd_first_order_workspace(p) bytes, 16-byte aligned;
+ *              solattn_fwd_first_order_workspace(p) bytes, 256-byte aligned;
  *              its contents on entry do not matter and are overwritten (the
- *              selection bitmaps, the per-row denominators and O in float32,
- *              passed between the two kernels of the call)
+ *              fused kernel's work-queue counters, and the selection
+ *              bitmaps, the per-row denominators and O in float32, passed
+ *              between the two kernels of the call)
  * Two kernels: the fused forward writes float32 O, its log denominators and
  * the bitmaps to the workspace; a second kernel adds the first-order terms
  * (an MFMA product C_j^T q_r per query row and unselected block: 2 n_i d^2
  * FLOPs per block pair) and rounds O to bf16 once.  Calls that share a
  * workspace race.  SOLATTN_FLAG_EXACT_ONLY is refused
  * (SOLATTN_E_INVALID_ARG): the first-order term extends the zeroth-order
- * one.  A workspace smaller than required is SOLATTN_E_INVALID_ARG.  Same
- * limit as solattn_fwd (N <= 8192).
+ * one.  A workspace that is NULL, misaligned or smaller than required is
+ * SOLATTN_E_WORKSPACE.  Same limit as solattn_fwd (N <= 8192).
  *
  * solattn_fwd_first_order_workspace: the workspace size in bytes; 0 for an
  * empty or invalid problem.
@@ -213,8 +236,11 @@ int solattn_fwd_first_order(const solattn_problem_t* p, const void* q, const voi
                             void* workspace, size_t workspace_bytes, void* stream);
 /*
  * Dense softmax attention softmax(scale * Q K^T) V on the same MFMA core,
- * block by block with one online softmax (no routing).  beta, chunk and
- * flags are ignored; block picks the tile size.
+ * block by block with one online softmax (no routing).  This is an in-house
+ * comparison point with no definition on the page (the page compares with
+ * dense FlashAttention-3 on its own hardware); it is textbook attention, the
+ * limit beta = -inf of the method.  beta, chunk and flags are ignored; block
+ * picks the tile size.
  *   q, k, v in: bf16 [B, H, L, d];  out: bf16 [B, H, L, d]
  */
 int solattn_dense_fwd(const solattn_problem_t* p, const void* q, const void* k, const void* v,

@@ -33,7 +33,9 @@ Pins (tests/test_oracle_*.py, CPU only):
                        hand-worked example in tests/golden
   forward_streaming    equals forward for every chunk size (C-invariance)
   dense                torch SDPA
-  approx denominator   Jensen bound against the exact block denominator
+  approx denominator   Jensen bound: never above the exact denominator, strictly
+                       below it for non-constant keys, equal for block-constant
+                       keys (read off the outputs with a one-block value probe)
   select_topk          k largest by construction (count, order and tie
                        invariants); with per-row counts |S_i| it reproduces
                        threshold routing, whose sets are upper sets of the row
@@ -48,6 +50,9 @@ Pins (tests/test_oracle_*.py, CPU only):
                        the output unchanged
   kv_moments           n_j times numpy's cross-covariance (np.cov, bias=True);
                        scale * q^T C_j equals first_order_terms' numerator
+  executed_flops       closed forms at all / none selected; equal to a
+                       token-by-token multiply-add count at partial selections
+                       with a ragged last block
 No function here is "parity unpinned".
 """
 

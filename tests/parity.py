@@ -18,7 +18,9 @@ Tolerances (from the task's parity rule for this method):
 
 from __future__ import annotations
 
+import json
 import math
+import os
 from dataclasses import dataclass
 from typing import Dict, Optional, Sequence
 
@@ -114,3 +116,34 @@ def check_pool(gpu: Dict[str, np.ndarray], q, k, v, r: ref.HeadResult, block: in
         tol = pool_tolerance(x, block, mean)
         err = np.abs(gpu[name].astype(np.float64) - want)
         assert np.all(err <= tol), f"{name}: max excess {(err - tol).max()}"
+
+
+def record(entry: dict) -> None:
+    """Append one JSON line describing a checked configuration (selection
+    counts and output errors) to the file named by SOLATTN_PARITY_REPORT,
+    when that variable is set; the tests' own assertions do not depend on it."""
+    path = os.environ.get("SOLATTN_PARITY_REPORT")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps(entry) + "\n")
+
+
+def summarise(config: str, beta: float, reps, extra=None) -> dict:
+    """One report entry from per-head reports (dicts with total, hard, flips,
+    tau_err_sigma and, where outputs were compared, max_abs and mean_rel)."""
+    out = [r for r in reps if "max_abs" in r]
+    e = {"config": config, "beta": beta if math.isfinite(beta) else str(beta),
+         "heads": len(reps),
+         "decisions": int(sum(r["total"] for r in reps)),
+         "hard_mismatches": int(sum(r["hard"] for r in reps)),
+         "in_band_flips": int(sum(r["flips"] for r in reps)),
+         "max_tau_err_sigma": float(max((r["tau_err_sigma"] for r in reps), default=0.0)),
+         "density": float(np.mean([r["density"] for r in reps])) if reps else 0.0,
+         "heads_with_outputs": len(out),
+         "max_abs": float(max((r["max_abs"] for r in out), default=0.0)),
+         "mean_rel": float(max((r["mean_rel"] for r in out), default=0.0))}
+    if extra:
+        e.update(extra)
+    record(e)
+    return e

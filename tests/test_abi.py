@@ -44,22 +44,24 @@ def test_problem_struct_layout_matches_header(sa):
 
 
 def test_version_and_strerror(sa):
-    assert sa.LIB.solattn_version() == 200
-    for code in (0, -1, -2, -3, 7):
+    assert sa.LIB.solattn_version() == 300
+    for code in (0, -1, -2, -3, -4, 7):
         assert isinstance(sa.LIB.solattn_strerror(code), bytes)
+    assert b"workspace" in sa.LIB.solattn_strerror(-4)
 
 
-FAKE = 1 << 20  # a 16-byte aligned address that is never dereferenced
+FAKE = 1 << 20  # a 256-byte aligned address that is never dereferenced
+WS = 1024        # solattn_fwd_workspace_bytes of every non-empty problem
 
 
-def call_fwd(sa, p, ptr=FAKE, **over):
+def call_fwd(sa, p, ptr=FAKE, ws_bytes=WS, **over):
     args = dict(q=ptr, k=ptr, v=ptr, qbar=ptr, kbar=ptr, vhat=ptr, tau=ptr, out=ptr,
-                sel_mask=None, sel_count=None)
+                workspace=ptr, sel_mask=None, sel_count=None)
     args.update(over)
     vals = [ctypes.c_void_p(args[n]) if args[n] is not None else None
-            for n in ("q", "k", "v", "qbar", "kbar", "vhat", "tau", "out", "sel_mask",
-                      "sel_count")]
-    return sa.LIB.solattn_fwd(ctypes.byref(p), *vals, None)
+            for n in ("q", "k", "v", "qbar", "kbar", "vhat", "tau", "out", "workspace",
+                      "sel_mask", "sel_count")]
+    return sa.LIB.solattn_fwd(ctypes.byref(p), *vals[:9], ws_bytes, *vals[9:], None)
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -79,6 +81,21 @@ def test_fwd_rejects_null_and_misaligned_pointers(sa, which):
     p = sa.problem(1, 2, 1000, 128, 128, 32, 1.0)
     assert call_fwd(sa, p, **{which: None}) == -1
     assert call_fwd(sa, p, **{which: FAKE + 8}) == -1
+
+
+def test_fwd_workspace_size_and_checks(sa):
+    p = sa.problem(1, 2, 1000, 128, 128, 32, 1.0)
+    assert sa.solattn_fwd_workspace_bytes(p) == WS
+    assert sa.solattn_fwd_workspace_bytes(sa.problem(0, 2, 1000, 128)) == 0
+    assert sa.solattn_fwd_workspace_bytes(sa.problem(1, 2, 1000, 96)) == 0
+    assert sa.LIB.solattn_fwd_workspace_bytes(None) == 0
+    assert call_fwd(sa, p, workspace=None) == -4
+    assert call_fwd(sa, p, workspace=FAKE + 16) == -4      # 16- but not 256-byte aligned
+    assert call_fwd(sa, p, ws_bytes=WS - 1) == -4
+    # argument errors are reported before workspace errors
+    assert call_fwd(sa, p, q=None, workspace=None) == -1
+    # an empty problem needs no workspace
+    assert call_fwd(sa, sa.problem(1, 0, 1000, 128), ptr=None, ws_bytes=0) == 0
 
 
 def test_fwd_rejects_misaligned_debug_outputs(sa):
@@ -168,23 +185,28 @@ def test_masked_forward_rejects_bad_arguments(sa):
     P = lambda x: ctypes.c_void_p(x)
     lib = sa.LIB
     # q, k, v, kbar, vhat, sel_in, out: each null or misaligned in turn
+    ws = [P(FAKE), WS]
     for i in range(7):
         args = [P(FAKE)] * 7
         args[i] = None
-        assert lib.solattn_fwd_masked(ctypes.byref(p), *args, None) == -1
+        assert lib.solattn_fwd_masked(ctypes.byref(p), *args, *ws, None) == -1
         args[i] = P(FAKE + 8)
-        assert lib.solattn_fwd_masked(ctypes.byref(p), *args, None) == -1
+        assert lib.solattn_fwd_masked(ctypes.byref(p), *args, *ws, None) == -1
     big = sa.problem(1, 1, 128 * 8193, 128, 128, 32, 1.0)
-    assert lib.solattn_fwd_masked(ctypes.byref(big), *([P(FAKE)] * 7), None) == -2
+    assert lib.solattn_fwd_masked(ctypes.byref(big), *([P(FAKE)] * 7), *ws, None) == -2
     empty = sa.problem(2, 0, 4096, 128, 128, 32, 1.0)
-    assert lib.solattn_fwd_masked(ctypes.byref(empty), *([None] * 7), None) == 0
+    assert lib.solattn_fwd_masked(ctypes.byref(empty), *([None] * 7), None, 0, None) == 0
+    # the workspace: missing, misaligned, too small
+    for bad in ([None, WS], [P(FAKE + 128), WS], [P(FAKE), WS - 4]):
+        assert lib.solattn_fwd_masked(ctypes.byref(p), *([P(FAKE)] * 7), *bad, None) == -4
 
 
 def test_first_order_workspace_size(sa):
     lib = sa.LIB
     p = sa.problem(2, 3, 1000, 128, 128, 32, 1.0)   # N = 8, one bitmap word per row
     up = lambda x: (x + 255) // 256 * 256
-    want = up(2 * 3 * 8 * 1 * 8) + up(2 * 3 * 1000 * 4) + up(2 * 3 * 1000 * 128 * 4)
+    # queue counters, bitmaps, log denominators, float32 O
+    want = WS + up(2 * 3 * 8 * 1 * 8) + up(2 * 3 * 1000 * 4) + up(2 * 3 * 1000 * 128 * 4)
     assert lib.solattn_fwd_first_order_workspace(ctypes.byref(p)) == want
     assert sa.solattn_fwd_first_order_workspace(p) == want
     assert lib.solattn_fwd_first_order_workspace(ctypes.byref(sa.problem(0, 3, 1000, 128))) == 0
@@ -205,11 +227,11 @@ def test_first_order_entry_points_reject_bad_arguments(sa):
     for i in range(10):   # each pointer null, then misaligned
         ptrs = [P(FAKE)] * 10
         ptrs[i] = None
-        assert fo(p, ptrs) == -1, i
+        assert fo(p, ptrs) == (-4 if i == 9 else -1), i
         ptrs[i] = P(FAKE + 8)
-        assert fo(p, ptrs) == -1, i
+        assert fo(p, ptrs) == (-4 if i == 9 else -1), i
     ok = [P(FAKE)] * 10
-    assert fo(p, ok, need - 1) == -1                        # workspace too small
+    assert fo(p, ok, need - 1) == -4                        # workspace too small
     exact = sa.problem(1, 2, 4096, 128, 128, 32, 1.0, exact_only=True)
     assert fo(exact, ok) == -1                              # exact-only is refused
     nan = sa.problem(1, 2, 4096, 128, 128, 32, math.nan)

@@ -70,7 +70,7 @@ def run_both(sa, q, k, v, beta, block, chunk=16, want_kvc=False):
     out1 = torch.empty_like(q)
     sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
     sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma)
-    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out0, ws.sel_mask,
+    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out0, ws.queue, ws.sel_mask,
                    ws.sel_count)
     sa.solattn_kv_moments(p, k, v, ws.kbar, ws.vhat, fws.kvc)
     sa.solattn_fwd_first_order(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, fws.kvc, ws.tau, out1,

@@ -57,7 +57,7 @@ def run_gpu(sa, q, k, v, beta, block, chunk, exact_only=False, scale=None):
     out = torch.empty_like(q)
     sa.solattn_pool(p, q, k, v, ws.qbar, ws.kbar, ws.vhat)
     sa.solattn_moments(p, ws.qbar, ws.kbar, ws.kmean, ws.kcov, ws.tau, ws.mu, ws.sigma)
-    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.sel_mask,
+    sa.solattn_fwd(p, q, k, v, ws.qbar, ws.kbar, ws.vhat, ws.tau, out, ws.queue, ws.sel_mask,
                    ws.sel_count)
     torch.cuda.synchronize()
     N = sa.num_blocks(L, block)
@@ -99,8 +99,8 @@ def check_head(g, q, k, v, beta, block, exact_only=False, scale=None, rows=None,
                                           exact_only)
         got = g["out"]
     max_abs, mean_rel, finite = parity.output_errors(got, want)
-    rep = dict(tag=tag, density=float(g["sel"].mean()), flips=st.in_band, max_abs=max_abs,
-               mean_rel=mean_rel, tau_err_sigma=tau_err)
+    rep = dict(tag=tag, density=float(g["sel"].mean()), flips=st.in_band, total=st.total,
+               hard=st.hard, max_abs=max_abs, mean_rel=mean_rel, tau_err_sigma=tau_err)
     log(f"  {tag}: {rep}")
     assert finite, f"{tag}: non-finite output"
     assert max_abs <= parity.MAX_ABS, f"{tag}: max-abs {max_abs}"
@@ -111,10 +111,13 @@ def check_head(g, q, k, v, beta, block, exact_only=False, scale=None, rows=None,
 def check_all_heads(sa, w: synth.Workload, beta, chunk=None, exact_only=False, scale=None):
     q, k, v = synth.make_inputs(w)
     g = run_gpu(sa, q, k, v, beta, w.block, chunk or w.chunk, exact_only, scale)
+    reps = []
     for b in range(w.B):
         for h in range(w.H):
-            check_head(head_view(g, b, h), q[b, h], k[b, h], v[b, h], beta, w.block, exact_only,
-                       scale, tag=f"{w.name} b{b} h{h} beta={beta}")
+            reps.append(check_head(head_view(g, b, h), q[b, h], k[b, h], v[b, h], beta, w.block,
+                                   exact_only, scale, tag=f"{w.name} b{b} h{h} beta={beta}"))
+    parity.summarise(f"{w.name}: B{w.B} H{w.H} L{w.L} d{w.d} block{w.block} "
+                     f"C{chunk or w.chunk}" + (" exact-only" if exact_only else ""), beta, reps)
     return g
 
 
@@ -260,16 +263,18 @@ def test_exact_only_at_the_beta_limits(sa):
     assert torch.count_nonzero(none).item() == 0
 
 
-def test_chunk_size_does_not_change_selection(sa):
+def test_chunk_size_does_not_change_the_result(sa):
+    # C is validated but does not change the schedule: the kernel routes 64
+    # pooled keys per step whatever C is, and the selected set is the union of
+    # the chunks' sets whatever the chunking (the page's streaming identity),
+    # so every output bit is the same for every C.
     w = synth.WORKLOADS["image"].replace(H=4)
     q, k, v = synth.make_inputs(w)
     base = run_gpu(sa, q, k, v, 1.0, w.block, 32)
-    for chunk in (1, 8, 16, 64):
+    for chunk in (1, 8, 16, 33, 64):
         g = run_gpu(sa, q, k, v, 1.0, w.block, chunk)
-        np.testing.assert_array_equal(g["sel"], base["sel"])
-        max_abs, mean_rel, _ = parity.output_errors(g["out"], base["out"].astype(np.float64))
-        log(f"  chunk {chunk}: max_abs={max_abs:.3g} mean_rel={mean_rel:.3g}")
-        assert max_abs <= 1e-2 and mean_rel <= 2e-3
+        for name in ("sel", "count", "out", "tau"):
+            np.testing.assert_array_equal(g[name], base[name], err_msg=f"chunk {chunk}: {name}")
 
 
 def test_repeat_calls_are_bitwise_identical(sa):
@@ -288,13 +293,29 @@ def sampled_rows(N, n=6):
     return sorted(r for r in rows if 0 <= r < N)[:n]
 
 
+_INPUTS = {}
+
+
+def full_size_inputs(w: synth.Workload):
+    """bf16 bit patterns of a full-size workload, kept for the next test that
+    asks for the same workload (several betas run on the same inputs)."""
+    key = repr(w)
+    if key not in _INPUTS:
+        _INPUTS.clear()
+        t0 = time.time()
+        _INPUTS[key] = synth.make_inputs_bf16_bits(w)
+        log(f"{w.name}: inputs generated in {time.time() - t0:.1f}s")
+    return _INPUTS[key]
+
+
 def full_size(sa, name, beta, heads_checked, n_rows=6):
-    """name: a workload name or a synth.Workload."""
+    """name: a workload name or a synth.Workload.
+
+    Every head: pooled arrays, thresholds and the whole selection against the
+    oracle; heads_checked: also n_rows sampled query blocks' outputs."""
     w = synth.WORKLOADS[name] if isinstance(name, str) else name
     name = w.name
-    t0 = time.time()
-    qb, kb, vb = synth.make_inputs_bf16_bits(w)
-    log(f"{name}: inputs generated in {time.time() - t0:.1f}s")
+    qb, kb, vb = full_size_inputs(w)
     q, k, v = bits_to_dev(qb), bits_to_dev(kb), bits_to_dev(vb)
     g = run_gpu(sa, q, k, v, beta, w.block, w.chunk)
     del q, k, v
@@ -313,17 +334,23 @@ def full_size(sa, name, beta, heads_checked, n_rows=6):
             # every head: pooling, thresholds and the whole selection
             r = ref.solattn_head(qh, kh, vh, beta, w.block, rows=[])
             parity.check_pool(gh, qh, kh, vh, r, w.block)
-            parity.check_stats(gh, r, beta)
+            tau_err = parity.check_stats(gh, r, beta)
             st = parity.selection_check(gh["sel"], r)
             assert st.hard == 0, f"{name} h{h}: {st.hard} hard selection mismatches"
+            reports.append(dict(density=float(gh["sel"].mean()), flips=st.in_band,
+                                total=st.total, hard=st.hard, tau_err_sigma=tau_err))
+    e = parity.summarise(f"{name}: B{w.B} H{w.H} L{w.L} d{w.d} block{w.block} C{w.chunk}", beta,
+                         reports, {"output_rows_per_head": n_rows})
+    log(f"{name} beta={beta}: {e}")
     return g, reports
 
 
 @pytest.mark.timeout(300)
-def test_wan_full_size(sa):
-    g, reps = full_size(sa, "wan", 1.0, heads_checked=(0, 13, 26, 39))
+@pytest.mark.parametrize("beta", [0.5, 1.0, 1.5])
+def test_wan_full_size(sa, beta):
+    g, reps = full_size(sa, "wan", beta, heads_checked=(0, 13, 26, 39))
     dens = g["sel"].mean()
-    log(f"wan density {dens:.4f} (Gaussian reference {0.5 * math.erfc(1 / math.sqrt(2)):.4f})")
+    log(f"wan density {dens:.4f} (Gaussian reference {0.5 * math.erfc(beta / math.sqrt(2)):.4f})")
 
 
 @pytest.mark.timeout(300)
@@ -332,8 +359,9 @@ def test_hunyuan_full_size(sa):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("beta", [-math.inf, 3.0])
+@pytest.mark.parametrize("beta", [-math.inf, 0.0, 1.0, 2.0, 3.0])
 def test_stress_full_size(sa, beta):
+    # heads 0-3 peaked (alpha = 4), heads 4-7 flat (iid): outputs on one of each
     full_size(sa, "stress", beta, heads_checked=(0, 7), n_rows=3)
 
 

@@ -49,6 +49,10 @@ def unit_block_weights(L, block):
     return np.ones_like(REAL["block_sizes"](L, block))
 
 
+def doubled_block_weights(L, block):
+    return 2 * REAL["block_sizes"](L, block)
+
+
 def first_order_sign(qi, kj, vj, centre, ref_max, scale):
     num, den = REAL["first_order_terms"](qi, kj, vj, centre, ref_max, scale)
     return -num, den
@@ -109,6 +113,8 @@ MUTANTS = {
     "no_block_weight": ("block_sizes", unit_block_weights, [
         lambda: P.test_block_constant_keys_make_the_approximation_exact(1.0),
         P.test_beta_plus_inf_is_attention_over_pooled_keys]),
+    "doubled_block_weight": ("block_sizes", doubled_block_weights, [
+        P.test_approx_denominator_is_below_the_exact_one]),
     "first_order_sign": ("first_order_terms", first_order_sign, [
         P.test_first_order_error_is_second_order_in_the_key_spread,
         P.test_hand_worked_example]),

@@ -205,6 +205,43 @@ def test_block_constant_keys_make_the_approximation_exact(beta):
     np.testing.assert_allclose(r.out, sdpa(q, k, v, r.scale), rtol=1e-10, atol=1e-12)
 
 
+def _denominator_probe(L=1000, block=64, constant_keys=False, beta=1.0):
+    """Outputs that expose the softmax denominator row by row.
+
+    Values are zero except on one selected block j0, whose tokens all carry
+    e_0.  Then coordinate 0 of every output row is the exact mass of block j0
+    divided by the row's whole denominator, for the oracle's forward
+    (approximate unselected blocks) and for dense attention alike, so their
+    ratio dense / oracle is D_approx / D_exact, row by row."""
+    w, q, k, _ = small(L=L, block=block)
+    if constant_keys:
+        rng = np.random.default_rng(5)
+        k = np.repeat(rng.standard_normal((w.N, w.d)), block, axis=0)[:L]
+    r = ref.solattn_head(q, k, np.zeros_like(q), beta, block)
+    sel = r.sel.copy()
+    j0 = 1
+    sel[:, j0] = True
+    v = np.zeros_like(q)
+    v[j0 * block:(j0 + 1) * block, 0] = 1.0
+    approx = ref.forward(q, k, v, sel, block, r.scale)[:, 0]
+    exact = ref.dense(q, k, v, r.scale)[:, 0]
+    return sel, exact / approx
+
+
+def test_approx_denominator_is_below_the_exact_one():
+    # Jensen: exp of a block's mean logit is at most the mean of exp over the
+    # block's logits, so n_j exp(scale q.Kbar_j) <= sum_c exp(scale q.k_c) for
+    # every unselected block, and the approximate denominator never exceeds
+    # the exact one; with non-constant keys the bound is strict.
+    sel, ratio = _denominator_probe()
+    assert (~sel).any(axis=1).all()
+    assert np.all(ratio <= 1.0 + 1e-12)
+    assert np.all(ratio < 1.0 - 1e-6)
+    # equality for block-constant keys (each block's logits are constant)
+    _, ratio_c = _denominator_probe(constant_keys=True)
+    np.testing.assert_allclose(ratio_c, 1.0, rtol=1e-12)
+
+
 def test_beta_plus_inf_is_attention_over_pooled_keys():
     # Nothing selected: each block contributes n_j exp(scale q.Kbar_j) and
     # exp(scale q.Kbar_j) Vhat_j, i.e. attention over the pooled keys with an
@@ -259,6 +296,44 @@ def test_executed_flops_counts():
     assert ref.executed_flops(L, d, b, sel) == 4.0 * L * L * d + 2.0 * L * d * N
     none = np.zeros((N, N), bool)
     assert ref.executed_flops(L, d, b, none) == 2.0 * L * d * N + 2.0 * L * d * N
+
+
+def _flops_by_enumeration(L, d, block, sel, exact_only=False):
+    """Multiply-adds counted one query token at a time (2 FLOPs each).
+
+    For every valid query token r of block i: d for q_r . k_c and d for
+    p_rc v_c, per key token c of each selected block; d per pooled key (all
+    N of them: the token-to-block tile); d per unselected block for the
+    p_rj Vhat_j product."""
+    N = ref.num_blocks(L, block)
+    macs = 0
+    for r in range(L):
+        i = r // block
+        for j in range(N):
+            macs += d  # tile entry q_r . Kbar_j
+            if sel[i, j]:
+                for c in range(j * block, min(L, (j + 1) * block)):
+                    macs += 2 * d
+            elif not exact_only:
+                macs += d
+    return 2.0 * macs
+
+
+@pytest.mark.parametrize("L,block", [(300, 64), (1000, 128), (129, 64)])
+def test_executed_flops_equal_enumeration_at_a_partial_selection(L, block):
+    # A partial selection with a ragged last block, selected for some query
+    # blocks and not for others (so n_i and n_j both differ from the block
+    # size somewhere): the closed form must equal the token-by-token count.
+    d = 32
+    N = ref.num_blocks(L, block)
+    rng = np.random.default_rng(L + block)
+    sel = rng.random((N, N)) < 0.4
+    sel[0, N - 1] = True
+    sel[N - 1, N - 1] = False
+    sel[N - 1, 0] = True
+    for eo in (False, True):
+        assert ref.executed_flops(L, d, block, sel, exact_only=eo) == \
+            _flops_by_enumeration(L, d, block, sel, exact_only=eo)
 
 
 def test_exact_only_with_nothing_selected_outputs_zero():
