@@ -7,6 +7,7 @@
 
 #include "solattn.h"
 #include "launch.hpp"
+#include "noalloc.hpp"
 
 namespace {
 
@@ -139,6 +140,31 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
   if (rc != SOLATTN_OK) return rc;
   return from_hip(solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, nullptr, out, sel_mask,
                                       sel_count, nullptr, nullptr, workspace,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int solattn_fwd_noalloc(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                        const float* qbar, const float* kbar, const float* vhat, const float* tau,
+                        void* out, uint64_t* sel_mask, int32_t* sel_count, void* stream) {
+  solattn::Shape s;
+  bool empty = false;
+  int rc = check_shape(p, &s, &empty);
+  if (rc != SOLATTN_OK) return rc;
+  rc = check_routing(p);
+  if (rc != SOLATTN_OK) return rc;
+  if (s.N > solattn::fused_max_blocks()) return SOLATTN_E_UNSUPPORTED;
+  if (empty) return SOLATTN_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(qbar) || !ok_ptr(kbar) ||
+      !ok_ptr(vhat) || !ok_ptr(tau) || !ok_ptr(out) || !ok_opt_ptr(sel_mask) ||
+      !ok_opt_ptr(sel_count))
+    return SOLATTN_E_INVALID_ARG;
+  // the scratch array must hold what solattn_fwd's workspace would
+  if (solattn::fwd_workspace_bytes() > solattn::noalloc_scratch_bytes())
+    return SOLATTN_E_WORKSPACE;
+  void* scratch = nullptr;
+  if (solattn::noalloc_scratch(&scratch) != hipSuccess) return SOLATTN_E_HIP;
+  return from_hip(solattn::launch_fwd(s, q, k, v, qbar, kbar, vhat, tau, nullptr, out, sel_mask,
+                                      sel_count, nullptr, nullptr, scratch,
                                       static_cast<hipStream_t>(stream)));
 }
 

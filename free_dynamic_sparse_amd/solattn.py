@@ -26,7 +26,7 @@ SOLATTN_E_WORKSPACE = -4
 SOLATTN_FLAG_EXACT_ONLY = 1
 
 EXPORTS = ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_workspace_bytes",
-           "solattn_fwd_masked", "solattn_dense_fwd",
+           "solattn_fwd_noalloc", "solattn_fwd_masked", "solattn_dense_fwd",
            "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp",
            "solattn_kv_moments", "solattn_fwd_first_order", "solattn_fwd_first_order_workspace",
            "solattn_strerror", "solattn_version")
@@ -59,6 +59,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.solattn_moments.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp,
                                 vp]
+    lib.solattn_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.solattn_fwd_workspace_bytes.argtypes = [pp]
     lib.solattn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.solattn_dense_fwd.argtypes = [pp, vp, vp, vp, vp, vp]
@@ -71,7 +72,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.solattn_fwd_first_order_workspace.restype = ctypes.c_size_t
     lib.solattn_fwd_first_order.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             ctypes.c_size_t, vp]
-    for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_masked",
+    for name in ("solattn_pool", "solattn_moments", "solattn_fwd", "solattn_fwd_noalloc",
+                 "solattn_fwd_masked",
                  "solattn_dense_fwd", "solattn_proxy_map", "solattn_select_topk", "solattn_select_topp",
                  "solattn_kv_moments", "solattn_fwd_first_order"):
         getattr(lib, name).restype = ctypes.c_int
@@ -183,6 +185,26 @@ def solattn_fwd(p: Problem, q, k, v, qbar, kbar, vhat, tau, out, workspace, sel_
     _check(LIB.solattn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar), _ptr(kbar),
                            _ptr(vhat), _ptr(tau), _ptr(out), _ptr(workspace), workspace.numel(),
                            _ptr(sel_mask), _ptr(sel_count), _stream(stream)), "solattn_fwd")
+
+
+def solattn_fwd_noalloc(p: Problem, q, k, v, qbar, kbar, vhat, tau, out, sel_mask=None,
+                        sel_count=None, stream=None) -> None:
+    """solattn_fwd with the library's own per-device scratch array instead of
+    a workspace (no allocation in the call; overlapping calls on one GPU race)."""
+    full, pooled, N = _dims(p)
+    B, H = p.batch, p.heads
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, torch.bfloat16, full, n)
+    for t, n in ((qbar, "qbar"), (kbar, "kbar"), (vhat, "vhat")):
+        _need(t, torch.float32, pooled, n)
+    _need(tau, torch.float32, (B, H, N), "tau")
+    if sel_mask is not None:
+        _need(sel_mask, torch.int64, (B, H, N, (N + 63) // 64), "sel_mask")
+    if sel_count is not None:
+        _need(sel_count, torch.int32, (B, H, N), "sel_count")
+    _check(LIB.solattn_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(qbar),
+                                   _ptr(kbar), _ptr(vhat), _ptr(tau), _ptr(out), _ptr(sel_mask),
+                                   _ptr(sel_count), _stream(stream)), "solattn_fwd_noalloc")
 
 
 def solattn_fwd_masked(p: Problem, q, k, v, kbar, vhat, sel_in, out, workspace,

@@ -161,6 +161,22 @@ int solattn_fwd(const solattn_problem_t* p, const void* q, const void* k, const 
  * none. */
 size_t solattn_fwd_workspace_bytes(const solattn_problem_t* p);
 
+/*
+ * solattn_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels, arguments and results, with the work-queue counters in a
+ * file-scope device array of the library (1 KiB, the most solattn_fwd's
+ * workspace ever needs; each GPU the library runs on holds one copy until
+ * the process ends) instead of a caller's workspace.  A problem needing more
+ * would return SOLATTN_E_WORKSPACE.  The call allocates and frees nothing;
+ * the caller still passes every input and output.  Every call on one GPU
+ * shares that GPU's array, which the call clears in-stream before use:
+ * calls that overlap on one GPU (different streams, or concurrent host
+ * threads) race and must be serialised by the caller.
+ */
+int solattn_fwd_noalloc(const solattn_problem_t* p, const void* q, const void* k, const void* v,
+                        const float* qbar, const float* kbar, const float* vhat, const float* tau,
+                        void* out, uint64_t* sel_mask, int32_t* sel_count, void* stream);
 
 /*
  * The fused forward with the selected sets given instead of routed: the
