@@ -610,7 +610,7 @@ def main() -> int:
         "pool_hbm_gbps": pool_bytes / (t["pool_ms"] * 1e-3) / 1e9,
         "moments_us": t["moments_ms"] * 1e3,
         "moments_gbps": moments_bytes / (t["moments_ms"] * 1e-3) / 1e9,
-        "roofline": {"bound": "mfma", "kernel": f"attn_kernel<{d},{w.block},fused> (solattn_fwd)",
+        "roofline": {"bound": "mfma", "kernel": f"attn_fused_kernel<{d},{w.block}> (solattn_fwd)",
                      "achieved": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": fwd_flops / (t["fwd_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
