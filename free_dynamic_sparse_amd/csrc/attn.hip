@@ -18,7 +18,7 @@
 // The nested loop of Algorithm 3.2, reordered for latency (the selected set
 // is the union of the chunks' sets, so the order changes nothing):
 //   * routing and approximation, one pass over the pooled keys, 64 at a
-//     time: the float32 rows of Kbar and Vhat are loaded once (whole
+//     time (32 with 64-token blocks): the float32 rows of Kbar and Vhat are loaded once (whole
 //     128-byte lines per instruction, the next 64 rows in flight meanwhile);
 //     the routing scores shat_ij = scale * Qbar_i . Kbar_j are formed from
 //     them in float32 for both query blocks and tested against the
@@ -73,7 +73,9 @@ struct Cfg {
   static constexpr int TILE = BLK * ROW;    // bytes per K or V tile
   static constexpr int DMA = TILE / 1024 / WAVES;  // 1 KB loads per wave per tile
   static constexpr int ROWS_1K = 1024 / ROW;       // tile rows per 1 KB load
-  static constexpr int SUB = 64;            // pooled rows staged at a time
+  // pooled rows staged at a time: a K tile holds two sub-chunks (the high
+  // bf16 parts of one, the low parts in its second half)
+  static constexpr int SUB = BLK >= 128 ? 64 : 32;
   // One LDS array: K tiles first so that every K read address fits the
   // 16-bit instruction offset, then V tiles, then the routing state.
   static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
@@ -671,7 +673,8 @@ __device__ __forceinline__ void approx_sub(const char* kt, const char* klo, cons
   l_run += lsum;
 }
 
-// The outer loop over the pooled keys, SUB = 64 at a time, for both query
+// The outer loop over the pooled keys, SUB at a time (64; 32 with 64-token
+// blocks, so that a K tile still holds a sub-chunk's high and low parts), for both query
 // blocks of the pair.  Per sub-chunk:
 //   * routing (Eq. 4 with the chunk-wise streaming test, Eqs. 6-7):
 //     shat_gj = scale * Qbar_g . Kbar_j >= tau_g in float32, with the dot
@@ -696,7 +699,9 @@ __device__ __forceinline__ void route_approx_phase(
     bool route, bool approx, bool grp_on, int grp, const bf16x8* qreg, float c, float& m_run,
     float& l_run, f32x16* o, int tid, int wave, int lane) {
   using C = Cfg<D, BLK>;
-  static_assert(C::SUB == 64 && C::SUB <= BLK, "a staged sub-chunk is one 64-bit word per group");
+  static_assert((C::SUB == 64 || C::SUB == 32) && 2 * C::SUB <= BLK,
+                "a staged sub-chunk is one or two 32-bit words per group");
+  constexpr int HALVES = C::SUB / 32;
   using Stage = PooledStage<D, BLK>;
   const uint32_t nsub = (N + C::SUB - 1) / C::SUB;
   uint8_t* const bits0 = reinterpret_cast<uint8_t*>(bits[0]);
@@ -715,17 +720,16 @@ __device__ __forceinline__ void route_approx_phase(
     if (sb + 1 < nsub) st.load(kbar_h, vhat_h, (sb + 1) * C::SUB, N, tid);
     __syncthreads();  // staged rows and their bits visible; the other buffer's readers are done
     if (approx && grp_on) {
-      const uint32_t rem = N - sb * C::SUB;
-      const uint64_t valid = rem >= 64u ? ~0ull : ((1ull << rem) - 1ull);
-      const uint32_t lo = __builtin_amdgcn_readfirstlane(bits[grp][2 * sb]);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane(bits[grp][2 * sb + 1]);
-      const uint64_t unsel = valid & ~(((uint64_t)hi << 32) | lo);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const uint32_t u = (uint32_t)(unsel >> (32 * half));
+      for (int half = 0; half < HALVES; ++half) {
+        const uint32_t base = sb * C::SUB + 32 * half;
+        const uint32_t rem = base < N ? N - base : 0u;
+        const uint32_t valid = rem >= 32u ? ~0u : ((1u << rem) - 1u);
+        const uint32_t u =
+            valid & ~__builtin_amdgcn_readfirstlane(bits[grp][sb * HALVES + half]);
         if (u)
-          approx_sub<D, BLK>(kt, klo, vt - C::V0, off, qreg, half, u, sb * C::SUB + 32 * half,
-                             N, n_last, c, m_run, l_run, o, lane);
+          approx_sub<D, BLK>(kt, klo, vt - C::V0, off, qreg, half, u, base, N, n_last, c, m_run,
+                             l_run, o, lane);
       }
     }
     buf ^= 1;
@@ -944,9 +948,17 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
   if (wq != nullptr && tid == 0) *next_slot = next;
 }
 
+// Both attention kernels are held to 256 registers per lane (two waves per
+// SIMD): with 64-token blocks a workgroup has only four waves, one per SIMD,
+// and without the cap the compiler spends the whole register file on one wave
+// per SIMD, leaving no second wave to overlap one wave's softmax with the
+// other's MFMAs (measured at the Wan shape with 64-token blocks: fused 31.7 ->
+// 20.8 ms, dense 145 -> 106 ms, outputs bitwise equal).
+
 // The dense comparison kernel: one workgroup per item, head-striped.
 template <int D, int BLK>
-__global__ __launch_bounds__(4 * BLK) void attn_dense_kernel(AttnArgs a) {
+__global__ __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_dense_kernel(AttnArgs a) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_DENSE];
   uint32_t bh, pair;
@@ -957,7 +969,8 @@ __global__ __launch_bounds__(4 * BLK) void attn_dense_kernel(AttnArgs a) {
 // The fused Sol-Attn kernel: persistent workgroups draining the work queues.
 // Each item hands the next one to the whole workgroup through LDS at its end.
 template <int D, int BLK>
-__global__ __launch_bounds__(4 * BLK) void attn_fused_kernel(AttnArgs a) {
+__global__ __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_fused_kernel(AttnArgs a) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_FUSED + 16];
   uint32_t* slot = reinterpret_cast<uint32_t*>(smem + C::SMEM_FUSED);

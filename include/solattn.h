@@ -62,8 +62,8 @@ extern "C" {
  *                         thresholding: the selected set is the union of
  *                         the chunks' sets).  Here it is validated and has
  *                         no other effect: the fused kernel routes 64 pooled
- *                         keys per step whatever its value, and every output
- *                         bit is the same for every C.
+ *                         keys per step (32 with 64-token blocks) whatever its
+ *                         value, and every output bit is the same for every C.
  *  beta                   standardized cutoff of tau_i = mu_i + beta*sigma_i
  *                         (Eq. 4).  Any finite value; -INFINITY selects every
  *                         block, +INFINITY none.  NaN is rejected.
@@ -140,7 +140,8 @@ int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* 
  *   sel_mask   out, may be NULL: u64 [B, H, N, ceil(N/64)]; bit (j mod 64) of
  *              word j/64 of row (b, h, i) is set iff block j is in S_i.
  *   sel_count  out, may be NULL: i32 [B, H, N], |S_i|.
- * For query block i the kernel scans the pooled keys 64 at a time: the
+ * For query block i the kernel scans the pooled keys 64 at a time (32 with
+ * 64-token blocks): the
  * proxy score shat_ij = scale*Qbar_i.Kbar_j is compared with tau_i on chip;
  * selected blocks get exact attention, unselected blocks the zeroth-order
  * term (n_j * exp(centre) in the denominator, exp(centre) * Vhat_j in the
