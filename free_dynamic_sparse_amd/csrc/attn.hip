@@ -538,13 +538,24 @@ struct PooledStage {
   __device__ __forceinline__ void load(const float* kbar_h, const float* vhat_h, uint32_t jb,
                                        uint32_t N, int tid) {
     const int row = tid / TPR, q = tid % TPR;
+    typedef const __attribute__((address_space(1))) f32x4 gf32x4;
+    if (jb + C::SUB <= N) {
+      // every staged row exists (all sub-chunks but possibly the last)
+#pragma unroll
+      for (int c = 0; c < F4; ++c) {
+        const size_t g = (size_t)(jb + row) * D + 4 * (q + TPR * c);
+        k[c] = *(gf32x4*)(kbar_h + g);
+        v[c] = *(gf32x4*)(vhat_h + g);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < F4; ++c) {
       f32x4 kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       if (jb + row < N) {
         const size_t g = (size_t)(jb + row) * D + 4 * (q + TPR * c);
-        kk = *reinterpret_cast<const f32x4*>(kbar_h + g);
-        vv = *reinterpret_cast<const f32x4*>(vhat_h + g);
+        kk = *(gf32x4*)(kbar_h + g);
+        vv = *(gf32x4*)(vhat_h + g);
       }
       k[c] = kk;
       v[c] = vv;
@@ -608,19 +619,28 @@ struct PooledStage {
       const int d = 4 * (q + TPR * c);
       const int byte = (d % 8) * 2;
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      auto pack4 = [](f32x4 x) {
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      // two floats to one packed pair (RNE), one conversion instruction
+      auto pack2 = [](float a, float b) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+      };
+      auto pack4 = [&](f32x4 x) {
         u32x2 r;
-        r[0] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[0]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[1]) << 16);
-        r[1] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[2]) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x[3]) << 16);
+        r[0] = pack2(x[0], x[1]);
+        r[1] = pack2(x[2], x[3]);
         return r;
       };
+      // high parts, and the low parts x - high from the packed high bits
+      const u32x2 hi = pack4(k[c]);
       f32x4 low;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) low[e] = k[c][e] - (float)(bf16)k[c][e];
+      for (int e = 0; e < 2; ++e) {
+        low[2 * e] = k[c][2 * e] - __uint_as_float(hi[e] << 16);
+        low[2 * e + 1] = k[c][2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u);
+      }
       const int koff = row * C::ROW + ((d / 8) ^ swz_k<C::SEGS>(row)) * 16 + byte;
-      *reinterpret_cast<u32x2*>(kt + koff) = pack4(k[c]);
+      *reinterpret_cast<u32x2*>(kt + koff) = hi;
       *reinterpret_cast<u32x2*>(klo + koff) = pack4(low);
       *reinterpret_cast<u32x2*>(vt + row * C::ROW + ((d / 8) ^ swz_v<C::SEGS>(row)) * 16 + byte) =
           pack4(v[c]);
@@ -645,13 +665,15 @@ __device__ __forceinline__ void approx_sub(const char* kt, const char* klo, cons
   using C = Cfg<D, BLK>;
   const int h = lane / 32;
   f32x16 t = score_tile_add<D, BLK>(klo, off, qreg, half, score_tile<D, BLK>(kt, off, qreg, half));
-  // register r of this lane holds staged row 4 h + kRow[r]; with the lane's
-  // bits pre-shifted, every test below is against a compile-time position
-  const uint32_t uh = unsel >> (4 * h);
+  // register r of lane l holds staged row 8 (r / 4) + 4 (l / 32) + r % 4:
+  // its unselected bit, for both halves of the wave, as a wave-uniform lane
+  // mask (scalar work), applied with one select per register
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    if (!((uh >> (8 * (r / 4) + r % 4)) & 1u)) t[r] = -INFINITY;
+    const int pos = 8 * (r / 4) + r % 4;
+    const uint32_t lo = 0u - ((unsel >> pos) & 1u), hi = 0u - ((unsel >> (pos + 4)) & 1u);
+    if (!__builtin_amdgcn_inverse_ballot_w64(((uint64_t)hi << 32) | lo)) t[r] = -INFINITY;
     mx = fmaxf(mx, t[r]);
   }
   mx = wave_max_pair(mx);
@@ -829,7 +851,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
   for (int ks = 0; ks < C::KS; ++ks) {
     u32x4 w = {0u, 0u, 0u, 0u};
     if (qrow < n_i)
-      w = *reinterpret_cast<const u32x4*>(qh + ((size_t)i_g * BLK + qrow) * D + 16 * ks + 8 * h);
+      w = *gbl(reinterpret_cast<const u32x4*>(qh + ((size_t)i_g * BLK + qrow) * D + 16 * ks +
+                                              8 * h));
     qreg[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
@@ -846,12 +869,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
     const bool route = a.sel_in == nullptr;
     float tau0 = INFINITY, tau1 = INFINITY;
     if (route) {
-      tau0 = a.tau[item0];
-      tau1 = pair1_on ? a.tau[item0 + 1] : INFINITY;
+      tau0 = gbl(a.tau)[item0];
+      tau1 = pair1_on ? gbl(a.tau)[item0 + 1] : INFINITY;
       for (int cc = tid; cc < 2 * D; cc += C::NT) {
         const int gq = cc / D;
         qbar_s[gq][cc % D] =
-            (gq == 0 || pair1_on) ? a.qbar[(size_t)(item0 + gq) * D + cc % D] : 0.f;
+            (gq == 0 || pair1_on) ? gbl(a.qbar)[(size_t)(item0 + gq) * D + cc % D] : 0.f;
       }
     } else {
       // masked mode: the two query blocks' given rows, with any bit at or
@@ -859,7 +882,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
       const uint32_t W64 = (N + 63) / 64;
       for (uint32_t e = tid; e < 2 * W64; e += C::NT) {
         const uint32_t gq = e / W64, w = e % W64;
-        uint64_t word = (gq == 0 || pair1_on) ? a.sel_in[(size_t)(item0 + gq) * W64 + w] : 0ull;
+        uint64_t word =
+            (gq == 0 || pair1_on) ? gbl(a.sel_in)[(size_t)(item0 + gq) * W64 + w] : 0ull;
         const uint32_t rows = N - 64 * w;
         if (rows < 64u) word &= (1ull << rows) - 1ull;
         selbits[gq][2 * w] = (uint32_t)word;
@@ -883,13 +907,13 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
         const uint32_t lo = selbits[grp][2 * w];
         const uint32_t hi = (2 * w + 1 < words) ? selbits[grp][2 * w + 1] : 0u;
         if (a.sel_mask)
-          a.sel_mask[(size_t)(bh * N + i_g) * W64 + w] = ((uint64_t)hi << 32) | lo;
+          gbl(a.sel_mask)[(size_t)(bh * N + i_g) * W64 + w] = ((uint64_t)hi << 32) | lo;
         count += __builtin_popcount(lo) + __builtin_popcount(hi);
       }
       if (a.sel_count) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) count += __shfl_xor(count, off);
-        if (lane == 0) a.sel_count[bh * N + i_g] = count;
+        if (lane == 0) gbl(a.sel_count)[bh * N + i_g] = count;
       }
     }
 
@@ -914,7 +938,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
   const float ltot = l_run + __shfl_xor(l_run, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (a.lse2 != nullptr && qrow < n_i && h == 0)
-    a.lse2[(size_t)bh * L + (size_t)i_g * BLK + qrow] = m_run + __builtin_amdgcn_logf(ltot);
+    gbl(a.lse2)[(size_t)bh * L + (size_t)i_g * BLK + qrow] = m_run + __builtin_amdgcn_logf(ltot);
   if (a.out_f32 != nullptr) {
     if (qrow < n_i) {
       float* orow = a.out_f32 + head + ((size_t)i_g * BLK + qrow) * D;
@@ -925,7 +949,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
           f32x4 st;
 #pragma unroll
           for (int e = 0; e < 4; ++e) st[e] = o[dt][4 * r4 + e] * inv;
-          *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * r4 + 4 * h) = st;
+          *gbl(reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * r4 + 4 * h)) = st;
         }
     }
   } else if (qrow < n_i) {
@@ -935,14 +959,16 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, char* smem, uint32_
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int d0 = 32 * dt + 8 * r4 + 4 * h;
-        const bf16 b0 = (bf16)(o[dt][4 * r4 + 0] * inv), b1 = (bf16)(o[dt][4 * r4 + 1] * inv);
-        const bf16 b2 = (bf16)(o[dt][4 * r4 + 2] * inv), b3 = (bf16)(o[dt][4 * r4 + 3] * inv);
-        uint2 st;
-        st.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-        st.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = st;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        u32x2 st;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const f32x2 pr = {o[dt][4 * r4 + 2 * e] * inv, o[dt][4 * r4 + 2 * e + 1] * inv};
+          st[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        }
+        *gbl(reinterpret_cast<u32x2*>(orow + d0)) = st;
       }
   }
   if (wq != nullptr && tid == 0) *next_slot = next;
@@ -979,11 +1005,26 @@ void attn_fused_kernel(AttnArgs a) {
   if (threadIdx.x == 0) slot[0] = wq.take(home);
   __syncthreads();
   uint32_t item = slot[0];
+  // The arguments are read again from the kernel-argument segment for every
+  // item (scalar loads, through a pointer the compiler cannot see to be loop
+  // invariant), so they are not held in scalar registers across the item
+  // loop; held there, they left too few for the item itself and about 46
+  // were spilled to vector-register lanes (measured: 16.76 -> 16.29 ms at the
+  // Wan shape, outputs bitwise equal).
+  typedef const __attribute__((address_space(4))) uint32_t KWord;
+  KWord* const kargs = (KWord*)__builtin_amdgcn_kernarg_segment_ptr();
+  static_assert(sizeof(AttnArgs) % 4 == 0, "the arguments are copied as whole words");
   while (item != kNoItem) {
-    const uint32_t bh = item / a.pairs;
+    KWord* kp = kargs;
+    asm volatile("" : "+s"(kp));
+    AttnArgs ai;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(AttnArgs) / 4); ++i)
+      reinterpret_cast<uint32_t*>(&ai)[i] = kp[i];
+    const uint32_t bh = item / ai.pairs;
     // slot[0] is rewritten only after this item's exact phase, which every
     // wave reaches after many barriers: by then all have read it
-    attn_item<D, BLK, true>(a, smem, bh, item - bh * a.pairs, &wq, home, slot);
+    attn_item<D, BLK, true>(ai, smem, bh, item - bh * ai.pairs, &wq, home, slot);
     __syncthreads();
     item = slot[0];
   }

@@ -45,6 +45,20 @@ __device__ __forceinline__ bool head_striped_item(uint32_t bid, uint32_t N, uint
   return *i < N;
 }
 
+// p as a global-memory pointer, so that accesses through it are global (not
+// flat) instructions: a pointer read from memory, such as the kernel arguments
+// the persistent kernel reloads per item, no longer carries that fact.  Flat
+// loads would also count against the LDS wait counter, so a wait for LDS
+// reads would wait for them too.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gbl(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gbl(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
