@@ -9,12 +9,18 @@
 // O(N d^2) without the N x N proxy map.
 //
 // Two small kernels, each with a fixed reduction order (deterministic):
-//   kcov_kernel    m = (1/N) sum_j Kbar_j and Sigma, one 32x32 tile of Sigma
-//                  per workgroup (which first forms the means of its 64
-//                  dimensions), float64 sums of centred products staged
-//                  through LDS
-//   tau_kernel     mu_i, sigma_i, tau_i; each thread keeps half a row of
-//                  Sigma in registers and the workgroup walks 32 query blocks
+//   kcov_kernel    m = (1/N) sum_j Kbar_j and Sigma: one 32x32 tile of Sigma
+//                  per workgroup, upper-triangle tiles only (each is also
+//                  written to its mirror, so Sigma is exactly symmetric).  The
+//                  workgroup first forms the means of its 64 dimensions
+//                  (float64 sums), then the d x d update of the centred
+//                  products as float64 MFMAs (v_mfma_f64_16x16x4f64: exact
+//                  products of the float32 centred values, float64 sums), one
+//                  16x16 sub-tile per wave, 4 pooled keys per MFMA
+//   tau_kernel     mu_i, sigma_i, tau_i for 32 query blocks per workgroup:
+//                  Y = Qbar Sigma by float32 MFMAs (v_mfma_f32_32x32x2f32,
+//                  one 32-column slab of Y per wave), then
+//                  sigma_i^2 = scale^2 sum_c Qbar_ic Y_ic in a fixed order
 
 #include <math.h>
 
@@ -24,93 +30,111 @@
 namespace solattn {
 namespace {
 
-// Sigma, one 32x32 tile per workgroup, and m.  The workgroup first forms the
-// means of its 32 row-dimensions and 32 column-dimensions (float64 sums over
-// the head's pooled keys in 8 fixed row phases, combined in a fixed order,
-// rounded to float32), then the centred products of those dimensions in
-// float64, staging 64 pooled keys at a time through LDS.  The diagonal tiles
-// also write m.  The head's pooled keys stay in L2 between the two passes.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// Upper-triangle tile y (row tile tr <= column tile tc) of a T x T tiling.
+__device__ __forceinline__ void upper_tile(int y, int T, int* tr, int* tc) {
+  int r = 0;
+  while (y >= T - r) {
+    y -= T - r;
+    ++r;
+  }
+  *tr = r;
+  *tc = r + y;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void kcov_kernel(const float* __restrict__ kbar,
                                                    float* __restrict__ kmean,
                                                    float* __restrict__ kcov, uint32_t N) {
-  constexpr int T = D / 32;  // tiles per dimension
-  constexpr int RB = 64;     // pooled keys staged per step
-  constexpr int PH = 256 / 32;  // row phases of the mean pass
+  constexpr int T = D / 32;   // 32-wide tiles per dimension
+  constexpr int PH = 4;       // row phases of the mean pass
+  constexpr int UNROLL = 8;   // rows (mean pass) or MFMA steps (update) in flight per thread
   const uint32_t bh = blockIdx.x;
-  const int r0 = 32 * (blockIdx.y / T);
-  const int c0 = 32 * (blockIdx.y % T);
+  int tr, tc;
+  upper_tile((int)blockIdx.y, T, &tr, &tc);
+  const int r0 = 32 * tr, c0 = 32 * tc;
   const float* src = kbar + (size_t)bh * N * D;
-  __shared__ float sr[RB][33];
-  __shared__ float sc[RB][33];
-  __shared__ double part[2][PH][32];
-  __shared__ float mr[32], mc[32];
+  __shared__ double part[PH][64];
+  __shared__ float mloc[64];  // means of dimensions r0 .. r0+31, then c0 .. c0+31
 
+  // ---- means: thread (phase, column) sums rows phase, phase + 4, ... in order
   {
-    const int ph = threadIdx.x / 32, col = threadIdx.x % 32;
-    double s_r = 0.0, s_c = 0.0;
-    for (uint32_t j = ph; j < N; j += PH) {
-      s_r += (double)src[(size_t)j * D + r0 + col];
-      s_c += (double)src[(size_t)j * D + c0 + col];
-    }
-    part[0][ph][col] = s_r;
-    part[1][ph][col] = s_c;
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const int which = threadIdx.x / 32;
-      double t = 0.0;
+    const int col = threadIdx.x % 64, ph = threadIdx.x / 64;
+    const float* p = src + (col < 32 ? r0 + col : c0 + col - 32);
+    double s = 0.0;
+    uint32_t j = ph;
+    for (; j + PH * (UNROLL - 1) < N; j += PH * UNROLL) {
+      float x[UNROLL];
 #pragma unroll
-      for (int q = 0; q < PH; ++q) t += part[which][q][col];
-      const float m = (float)(t / (double)N);
-      if (which == 0) {
-        mr[col] = m;
-        if (r0 == c0) kmean[(size_t)bh * D + r0 + col] = m;
-      } else {
-        mc[col] = m;
-      }
+      for (int u = 0; u < UNROLL; ++u) x[u] = p[(size_t)(j + PH * u) * D];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) s += (double)x[u];
     }
-    __syncthreads();
+    for (; j < N; j += PH) s += (double)p[(size_t)j * D];
+    part[ph][col] = s;
   }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    double t = 0.0;
+#pragma unroll
+    for (int q = 0; q < PH; ++q) t += part[q][threadIdx.x];
+    const float m = (float)(t / (double)N);
+    mloc[threadIdx.x] = m;
+    if (tr == tc && threadIdx.x < 32) kmean[(size_t)bh * D + r0 + threadIdx.x] = m;
+  }
+  __syncthreads();
 
-  const int ta = threadIdx.x / 16, tb = threadIdx.x % 16;
-  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-  for (uint32_t j0 = 0; j0 < N; j0 += RB) {
-    for (int e = threadIdx.x; e < RB * 32; e += 256) {
-      const int jj = e / 32, col = e % 32;
-      const uint32_t j = j0 + jj;
-      float vr = 0.f, vc = 0.f;
-      if (j < N) {
-        vr = src[(size_t)j * D + r0 + col] - mr[col];
-        vc = src[(size_t)j * D + c0 + col] - mc[col];
-      }
-      sr[jj][col] = vr;
-      sc[jj][col] = vc;
+  // ---- d x d update: wave w owns the 16x16 sub-tile (w / 2, w % 2) of the
+  // tile.  Per MFMA, lane l contributes the centred value of pooled key
+  // 4 s + l / 16 in row dimension dr (A operand, row l % 16, k = l / 16) and in
+  // column dimension dc (B operand, column l % 16, k = l / 16); keys past N
+  // contribute 0.
+  const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+  const int sr = w / 2, sc = w % 2, i16 = l % 16, kq = l / 16;
+  const int dr = r0 + 16 * sr + i16, dc = c0 + 16 * sc + i16;
+  const float mr = mloc[16 * sr + i16], mc = mloc[32 + 16 * sc + i16];
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  const uint32_t steps = (N + 3) / 4;
+  for (uint32_t s0 = 0; s0 < steps; s0 += UNROLL) {
+    float xa[UNROLL], xb[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      // keys past N read the last key (in bounds) and are then zeroed, so
+      // that every load of the group is in flight at once
+      const uint32_t j = 4 * (s0 + u) + kq;
+      const size_t jr = (size_t)(j < N ? j : N - 1) * D;
+      xa[u] = src[jr + dr];
+      xb[u] = src[jr + dc];
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int jj = 0; jj < RB; ++jj) {
-      const double a0 = sr[jj][2 * ta], a1 = sr[jj][2 * ta + 1];
-      const double b0 = sc[jj][2 * tb], b1 = sc[jj][2 * tb + 1];
-      acc[0][0] += a0 * b0;
-      acc[0][1] += a0 * b1;
-      acc[1][0] += a1 * b0;
-      acc[1][1] += a1 * b1;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const bool in = 4 * (s0 + u) + kq < N;
+      xa[u] = in ? xa[u] - mr : 0.f;
+      xb[u] = in ? xb[u] - mc : 0.f;
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[u], (double)xb[u], acc, 0, 0, 0);
   }
+  // result register e of lane l: column l % 16 and row l / 16 + 4 e of the
+  // sub-tile (the float64 MFMA's result layout, checked on the device)
   float* dst = kcov + (size_t)bh * D * D;
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-      dst[(size_t)(r0 + 2 * ta + x) * D + c0 + 2 * tb + y] = (float)(acc[x][y] / (double)N);
+  for (int e = 0; e < 4; ++e) {
+    const int row = r0 + 16 * sr + kq + 4 * e, col = c0 + 16 * sc + i16;
+    const float v = (float)(acc[e] / (double)N);
+    dst[(size_t)row * D + col] = v;
+    if (tr != tc) dst[(size_t)col * D + row] = v;
+  }
 }
 
-// mu_i, sigma_i and tau_i for 32 query blocks per workgroup.  Each thread
-// keeps half a row r of Sigma in registers and forms (Sigma Qbar_i)_r for the
-// 32 blocks; the per-dimension terms Qbar_ir (Sigma Qbar_i)_r and Qbar_ir m_r
-// go to LDS, and TPG threads per block then sum them over r in a fixed order
-// (a run of D / TPG dimensions each, then lane exchanges).
+// mu_i, sigma_i and tau_i for G = 32 query blocks per workgroup, D / 32 waves.
+// Wave w forms the slab Y[:, 32 w .. 32 w + 31] of Y = Qbar Sigma (A = the
+// blocks' Qbar rows from LDS, lane l holding block l % 32 and dimension
+// 2 s + l / 32; B = Sigma rows 2 s, 2 s + 1 from memory), multiplies it by the
+// matching Qbar entries and sums over its 32 columns (lane butterfly, fixed
+// order); the waves' partial sums are then added in wave order.
 template <int D>
 __global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kmean,
@@ -118,24 +142,14 @@ __global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qb
                                                     float* __restrict__ tau, float* __restrict__ mu,
                                                     float* __restrict__ sigma, uint32_t N,
                                                     float scale, float beta) {
-  constexpr int NT = 2 * D, HALF = D / 2, G = 32;
-  constexpr int TPG = NT / G;      // threads per query block in the final sums
-  constexpr int RUN = D / TPG;     // dimensions summed by each of them
-  static_assert(TPG * RUN == D && (TPG & (TPG - 1)) == 0, "reduction shape");
+  constexpr int NT = 2 * D, G = 32, W = D / 32;
   const uint32_t bh = blockIdx.x;
   const uint32_t i0 = blockIdx.y * G;
-  const int t = threadIdx.x, r = t / 2, h = t % 2;
+  const int t = threadIdx.x, w = t / 64, l = t % 64, h = l / 32, l32 = l % 32;
 
-  // half a row of Sigma per thread, kept in registers
-  float srow[HALF];
-  const float* cov = kcov + (size_t)bh * D * D + (size_t)r * D + h * HALF;
-#pragma unroll
-  for (int e = 0; e < HALF; ++e) srow[e] = cov[e];
-
-  __shared__ float qs[G][D];
+  __shared__ float qs[G][D + 1];
   __shared__ float ms[D];
-  __shared__ float pq[G][D + 1];  // Qbar_ir (Sigma Qbar_i)_r
-  __shared__ float pm[G][D + 1];  // Qbar_ir m_r
+  __shared__ float part[W][G];
   for (int e = t; e < G * D; e += NT) {
     const int g = e / D, c = e % D;
     const uint32_t i = i0 + g;
@@ -144,48 +158,50 @@ __global__ __launch_bounds__(2 * D) void tau_kernel(const float* __restrict__ qb
   for (int c = t; c < D; c += NT) ms[c] = kmean[(size_t)bh * D + c];
   __syncthreads();
 
-  for (int g = 0; g < G; ++g) {
-    const float* qv = qs[g];
-    float y = 0.f;
+  const float* cov = kcov + (size_t)bh * D * D + 32 * w + l32;
+  f32x16 acc;
 #pragma unroll
-    for (int e = 0; e < HALF; ++e) y = fmaf(srow[e], qv[h * HALF + e], y);
-    const float other = __shfl_xor(y, 1);
-    if (h == 0) {
-      pq[g][r] = (y + other) * qv[r];  // (Sigma Qbar)_r, the two halves in a fixed order
-      pm[g][r] = ms[r] * qv[r];
-    }
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < D / 2; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[l32][2 * s + h], cov[(size_t)(2 * s + h) * D],
+                                               acc, 0, 0, 0);
+  // lane l holds Y[i][c], c = 32 w + l % 32, i = mfma_row(r, l / 32)
+  const int c = 32 * w + l32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float v = acc[r] * qs[mfma_row(r, h)][c];
+#pragma unroll
+    for (int o = 16; o >= 1; o /= 2) v += __shfl_xor(v, o);
+    if (l32 == 0) part[w][mfma_row(r, h)] = v;
   }
   __syncthreads();
 
-  const int g = t / TPG, part = t % TPG;
-  float qf = 0.f, md = 0.f;
+  if (t < G) {
+    const uint32_t i = i0 + t;
+    float qf = 0.f;
 #pragma unroll
-  for (int e = 0; e < RUN; ++e) {
-    qf += pq[g][part * RUN + e];
-    md += pm[g][part * RUN + e];
-  }
-#pragma unroll
-  for (int o = TPG / 2; o >= 1; o /= 2) {
-    qf += __shfl_xor(qf, o);
-    md += __shfl_xor(md, o);
-  }
-  const uint32_t i = i0 + g;
-  if (part == 0 && i < N) {
-    const float mu_i = scale * md;
-    const float sigma_i = sqrtf(fmaxf(scale * scale * qf, 0.f));
-    float tau_i;
-    if (beta == -INFINITY)
-      tau_i = -INFINITY;
-    else if (beta == INFINITY)
-      tau_i = INFINITY;
-    else if (sigma_i == 0.f)
-      tau_i = -INFINITY;  // constant proxy row: every block passes the >= test
-    else
-      tau_i = mu_i + beta * sigma_i;
-    const size_t o = (size_t)bh * N + i;
-    tau[o] = tau_i;
-    if (mu) mu[o] = mu_i;
-    if (sigma) sigma[o] = sigma_i;
+    for (int x = 0; x < W; ++x) qf += part[x][t];
+    float md = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < D; ++r) md = fmaf(qs[t][r], ms[r], md);
+    if (i < N) {
+      const float mu_i = scale * md;
+      const float sigma_i = sqrtf(fmaxf(scale * scale * qf, 0.f));
+      float tau_i;
+      if (beta == -INFINITY)
+        tau_i = -INFINITY;
+      else if (beta == INFINITY)
+        tau_i = INFINITY;
+      else if (sigma_i == 0.f)
+        tau_i = -INFINITY;  // constant proxy row: every block passes the >= test
+      else
+        tau_i = mu_i + beta * sigma_i;
+      const size_t o = (size_t)bh * N + i;
+      tau[o] = tau_i;
+      if (mu) mu[o] = mu_i;
+      if (sigma) sigma[o] = sigma_i;
+    }
   }
 }
 
@@ -193,7 +209,8 @@ template <int D>
 hipError_t launch_moments_t(const Shape& s, const float* qbar, const float* kbar, float* kmean,
                             float* kcov, float* tau, float* mu, float* sigma, hipStream_t stream) {
   const uint32_t bh = (uint32_t)s.bh, N = (uint32_t)s.N;
-  hipLaunchKernelGGL((kcov_kernel<D>), dim3(bh, (D / 32) * (D / 32)), dim3(256), 0, stream, kbar,
+  constexpr int T = D / 32;
+  hipLaunchKernelGGL((kcov_kernel<D>), dim3(bh, T * (T + 1) / 2), dim3(256), 0, stream, kbar,
                      kmean, kcov, N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

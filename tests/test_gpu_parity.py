@@ -277,6 +277,18 @@ def test_chunk_size_does_not_change_the_result(sa):
             np.testing.assert_array_equal(g[name], base[name], err_msg=f"chunk {chunk}: {name}")
 
 
+def test_key_covariance_is_exactly_symmetric(sa):
+    # each off-diagonal 32x32 tile of Sigma is computed once and written to
+    # both halves; d = 128 (ten tiles) and d = 64 (three)
+    for wname, H in (("image", 3), ("tiny", 1)):
+        w = synth.WORKLOADS[wname].replace(H=H)
+        q, k, v = synth.make_inputs(w)
+        g = run_gpu(sa, q, k, v, 1.0, w.block, w.chunk)
+        cov = g["kcov"]
+        assert np.array_equal(cov, np.swapaxes(cov, -1, -2)), wname
+        assert np.all(np.isfinite(cov)), wname
+
+
 def test_repeat_calls_are_bitwise_identical(sa):
     w = synth.WORKLOADS["image"].replace(H=4)
     q, k, v = synth.make_inputs(w)
