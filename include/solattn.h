@@ -111,7 +111,8 @@ int solattn_pool(const solattn_problem_t* p, const void* q, const void* k, const
  *               without building the N x N map.
  * tau_i is -INFINITY when beta is -INFINITY or sigma_i == 0 (a constant row:
  * every block passes the >= test), +INFINITY when beta is +INFINITY.
- * Moments accumulate in float64.
+ * m and Sigma accumulate in float64 (Sigma is exactly symmetric); mu and sigma
+ * in float32.  Every sum has a fixed order, so results are deterministic.
  */
 int solattn_moments(const solattn_problem_t* p, const float* qbar, const float* kbar,
                     float* kmean, float* kcov, float* tau, float* mu, float* sigma,
