@@ -122,8 +122,11 @@ struct AttnArgs {
   int64_t L;
   uint32_t N;
   uint32_t pairs;    // ceil(N / 2)
-  uint32_t per_xcd;  // pairs per XCD slab: ceil(pairs / 8)
-  uint32_t queue_len;  // entries per work queue: B * H * per_xcd
+  uint32_t per_xcd;  // pairs per XCD slab (dense kernel): ceil(pairs / 8)
+  uint32_t queue_len;  // entries per work queue (fused kernel): ceil(runs / 8) * run
+  uint32_t run;        // pairs per run of the work queues
+  uint32_t runs_per_head;  // ceil(pairs / run)
+  uint32_t runs;       // B * H * runs_per_head
   float scale;
   float c_log2;      // scale * log2(e): logits enter exp2 in this unit
   uint32_t exact_only;
@@ -763,24 +766,32 @@ __device__ __forceinline__ void route_approx_phase(
 
 // ------------------------------------------------------------- work queue
 
-// Work items of the fused kernel are pairs of query blocks.  They are dealt
-// to kXcds queues in the head-striped order of head_striped_item (queue x
-// holds, head after head, the slab (x + bh) mod 8 of the head's pairs), so a
-// queue's items are neighbouring query blocks of one head at a time.  A
-// persistent workgroup of XCD x (workgroup id mod 8, the order in which the
-// dispatcher deals workgroups to XCDs) takes items from queue x with an
-// atomic counter, in order, and once that queue is empty from the others in
-// turn.  Query-dependent budgets make items unequal; a workgroup that
-// finishes early takes the next item at once, and no CU waits for a
-// workgroup to be dispatched.  An item is computed the same way wherever it
-// runs, so the output does not depend on which workgroup takes it.
+// Work items of the fused kernel are pairs of query blocks.  They are cut
+// into runs of `run` consecutive pairs of one head (twice the workgroups an
+// XCD holds, or the whole head if it has fewer pairs), and the runs, head
+// after head, are dealt round-robin to kXcds queues (run g to queue g mod 8),
+// so a queue's items are neighbouring query blocks of one head at a time and
+// the XCDs work on the same one or two heads at any moment.  A persistent
+// workgroup of XCD x (workgroup id mod 8, the order in which the dispatcher
+// deals workgroups to XCDs) takes items from queue x with an atomic counter,
+// in order, and once that queue is empty from the others in turn.
+// Query-dependent budgets make items unequal; a workgroup that finishes early
+// takes the next item at once, and no CU waits for a workgroup to be
+// dispatched.  Runs longer than the XCD's workgroup count keep more of the
+// items running at once on an XCD neighbours of each other, whose selected
+// key blocks overlap (an L2 model on Wan selections: hit rate 0.54 with one
+// slab of ceil(pairs / 8) per XCD and head, 0.59 with runs of 64).  An item
+// is computed the same way wherever it runs, so the output does not depend on
+// which workgroup takes it.
 constexpr uint32_t kQueueStride = 32;  // u32 between counters: one 128-byte line each
 constexpr uint32_t kNoItem = 0xFFFFFFFFu;
 
 struct WorkQueue {
   uint32_t* ctr;
-  uint32_t len;    // entries per queue (bh count * per)
-  uint32_t per;    // pairs per slab
+  uint32_t len;    // entries per queue: ceil(runs / 8) * run
+  uint32_t run;    // pairs per run
+  uint32_t rph;    // runs per head
+  uint32_t runs;   // runs in all
   uint32_t pairs;  // pairs per head
   // Next item (bh * pairs + pair) for a workgroup of XCD home, or kNoItem.
   __device__ uint32_t take(uint32_t home) const {
@@ -790,9 +801,11 @@ struct WorkQueue {
         const uint32_t idx = __hip_atomic_fetch_add(ctr + qx * kQueueStride, 1u,
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (idx >= len) break;
-        const uint32_t bh = idx / per, slot = idx - bh * per;
-        const uint32_t pair = ((qx + bh) % kXcds) * per + slot;
-        if (pair < pairs) return bh * pairs + pair;
+        const uint32_t k = idx / run, slot = idx - k * run;
+        const uint32_t g = qx + kXcds * k;  // the run this entry belongs to
+        if (g >= runs) break;               // and every later entry of this queue too
+        const uint32_t bh = g / rph, pair = (g - bh * rph) * run + slot;
+        if (pair < pairs) return bh * pairs + pair;  // else: past a head's last pair
       }
     }
     return kNoItem;
@@ -1000,7 +1013,7 @@ void attn_fused_kernel(AttnArgs a) {
   using C = Cfg<D, BLK>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM_FUSED + 16];
   uint32_t* slot = reinterpret_cast<uint32_t*>(smem + C::SMEM_FUSED);
-  const WorkQueue wq{a.queue, a.queue_len, a.per_xcd, a.pairs};
+  const WorkQueue wq{a.queue, a.queue_len, a.run, a.runs_per_head, a.runs, a.pairs};
   const uint32_t home = blockIdx.x % kXcds;
   if (threadIdx.x == 0) slot[0] = wq.take(home);
   __syncthreads();
@@ -1062,7 +1075,6 @@ hipError_t launch_attn(const Shape& s, AttnArgs a, hipStream_t stream) {
   a.N = (uint32_t)s.N;
   a.pairs = (uint32_t)((s.N + 1) / 2);
   a.per_xcd = (a.pairs + kXcds - 1) / kXcds;
-  a.queue_len = (uint32_t)(s.bh * a.per_xcd);
   a.scale = s.scale;
   a.c_log2 = s.scale * kLog2e;
   const uint64_t items = (uint64_t)s.bh * a.pairs;
@@ -1079,6 +1091,11 @@ hipError_t launch_attn(const Shape& s, AttnArgs a, hipStream_t stream) {
                                    Cfg<DD, BB>::NT, INST, &grid);                              \
     if (e != hipSuccess) return e;                                                             \
     if (items < grid) grid = (uint32_t)items;                                                  \
+    a.run = 2 * ((grid + kXcds - 1) / kXcds);                                                  \
+    if (a.run > a.pairs) a.run = a.pairs;                                                      \
+    a.runs_per_head = (a.pairs + a.run - 1) / a.run;                                           \
+    a.runs = (uint32_t)(s.bh * a.runs_per_head);                                               \
+    a.queue_len = (a.runs + kXcds - 1) / kXcds * a.run;                                        \
     hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(kWave), 0, stream, a.queue);          \
     e = hipGetLastError();                                                                     \
     if (e != hipSuccess) return e;                                                             \
