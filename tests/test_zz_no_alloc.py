@@ -82,3 +82,50 @@ def test_noalloc_forward_rejects_bad_arguments(sa):
     empty = sa.problem(1, 0, 1000, 128, 128, 32, 1.0)
     assert sa.LIB.solattn_fwd_noalloc(ctypes.byref(empty), *([None] * 8), None, None,
                                       None) == 0
+
+
+def test_noalloc_forward_replays_from_a_graph(sa):
+    # Code under graph capture is one of the callers this entry point is for:
+    # a captured call, replayed three times with cleared outputs, eager work
+    # and an eager allocation-free call on another problem (which shares the
+    # scratch array) between replays, equals the eager call bit for bit.
+    w = synth.Workload("noalloc_graph", B=1, H=4, L=3000, d=128, block=128, chunk=32, seed=43,
+                       kind="pos", grid=(1, 1, 3000))
+    other = synth.Workload("noalloc_other", B=1, H=2, L=1000, d=64, block=64, chunk=16, seed=44,
+                           kind="pos", grid=(1, 1, 1000))
+    p, q, k, v, ws = _prepare(sa, w, 1.0)
+    po, qo, ko, vo, wso = _prepare(sa, other, 0.5)
+    eager = torch.empty_like(q)
+    mask0, count0 = torch.zeros_like(ws.sel_mask), torch.zeros_like(ws.sel_count)
+    _noalloc_through_abi(sa, p, q, k, v, ws, eager, mask0, count0)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    mask, count = torch.zeros_like(ws.sel_mask), torch.zeros_like(ws.sel_count)
+    out_o = torch.empty_like(qo)
+    mask_o, count_o = torch.zeros_like(wso.sel_mask), torch.zeros_like(wso.sel_count)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager call on a side stream first
+        _noalloc_through_abi(sa, p, q, k, v, ws, out, mask, count)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _noalloc_through_abi(sa, p, q, k, v, ws, out, mask, count)
+    torch.cuda.synchronize()
+    noise = torch.randn(1 << 20, device="cuda")
+    for replay in range(3):
+        print(f"noalloc graph replay {replay}", flush=True)
+        out.zero_()
+        mask.zero_()
+        count.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {replay}: output"
+        assert torch.equal(mask, mask0), f"replay {replay}: selections"
+        assert torch.equal(count, count0), f"replay {replay}: counts"
+        noise.mul_(1.5).add_(0.25)  # eager work between replays
+        _noalloc_through_abi(sa, po, qo, ko, vo, wso, out_o, mask_o, count_o)
+        torch.cuda.synchronize()
+    assert 0 < count0.sum().item() < w.B * w.H * w.N * w.N
